@@ -1,0 +1,60 @@
+"""Oracle step 6: longest-processing-time-first (LPT) work list over tiles.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What the pages fix: once the mask exists each head's load (kept sparse blocks
+times the time per block) is known exactly, and the aim is to shorten the
+critical path left by a few heavy heads (aixai.ru FVAttn post, section
+"Runtime Load Balancing (RLB)"; PaperDaily FVAttn article, method section,
+where heavy heads are moved greedily from the busiest to the idlest rank).
+The pages balance heads across GPU ranks; on one GPU the same problem is the
+spread of (head, q-block) tiles over the persistent workgroups.  The pages do
+not describe this single-GPU schedule: it is a reading.
+
+Reading taken:
+  * tile t = h * nB + i has cost c_t = kv_count[h, i] (kept blocks);
+  * tiles are ordered by (cost descending, tile id ascending);
+  * in that order each tile goes to the worker with the smallest load so far,
+    the lowest worker index on ties (Graham's LPT rule), and is appended to
+    that worker's list;
+  * outputs: the order, per-worker lists concatenated in worker order with
+    offsets, and the final per-worker loads.
+One schedule is correct per input.
+
+Pins (tests/test_oracle_lpt.py): a hand-worked two-worker example,
+conservation, Graham's 4/3 - 1/(3W) bound against the brute-force optimum,
+the makespan <= mean + max-cost bound, W = 1 and W >= tiles.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def lpt_order(costs: np.ndarray) -> np.ndarray:
+    costs = np.asarray(costs, dtype=np.int64)
+    t = np.arange(costs.shape[0])
+    return np.lexsort((t, -costs)).astype(np.int32)
+
+
+def lpt_schedule(costs: np.ndarray, n_workers: int):
+    """Greedy LPT.  Returns (order, worker_offsets, worker_tiles, worker_load)."""
+    if n_workers < 1:
+        raise ValueError("n_workers must be >= 1")
+    costs = np.asarray(costs, dtype=np.int64).reshape(-1)
+    order = lpt_order(costs)
+    loads = np.zeros(n_workers, dtype=np.int64)
+    lists = [[] for _ in range(n_workers)]
+    for t in order:
+        w = int(np.argmin(loads))          # argmin returns the lowest index on ties
+        lists[w].append(int(t))
+        loads[w] += costs[t]
+    sizes = np.array([len(x) for x in lists], dtype=np.int64)
+    offsets = np.zeros(n_workers + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(sizes)
+    tiles = np.array([t for x in lists for t in x], dtype=np.int32)
+    return order, offsets, tiles, loads
+
+
+def predicted_imbalance(loads: np.ndarray) -> float:
+    loads = np.asarray(loads, dtype=np.float64)
+    return float(loads.max() / loads.mean()) if loads.mean() > 0 else 1.0
