@@ -1,0 +1,204 @@
+"""ctypes binding of libfvattn.so.
+
+Argument marshalling only: every function takes torch tensors (device memory
+allocated by the caller), checks dtype / shape / contiguity, and passes raw
+pointers plus torch's current HIP stream to the C entry point of the same
+name.  All compute happens in the library's HIP kernels; if the library is
+missing this module raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB_PATH = os.path.join(PKG, "libfvattn.so")
+HEADER = os.path.join(ROOT, "include", "fvattn.h")
+
+OK, EINVAL, EUNSUPPORTED, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+
+_c_void_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_float = ctypes.c_float
+_c_size_t = ctypes.c_size_t
+
+_SIGNATURES = {
+    "fvattn_status_string": (ctypes.c_char_p, [_c_int]),
+    "fvattn_version": (_c_int, []),
+    "fvattn_hilbert_permute": (_c_int, [_c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                        _c_void_p]),
+    "fvattn_permute_rows": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                     _c_int, _c_int, _c_void_p]),
+    "fvattn_route_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
+    "fvattn_route": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                              _c_int, _c_float, _c_int, _c_void_p, _c_void_p,
+                              _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
+                              _c_void_p]),
+    "fvattn_schedule_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int]),
+    "fvattn_schedule": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p,
+                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_size_t, _c_void_p]),
+    "fvattn_sparse_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_float, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_void_p, _c_int, _c_void_p, _c_void_p]),
+}
+
+
+class FvattnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree libfvattn.so (built by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it first "
+                              "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def declared_symbols() -> list:
+    """Entry points declared in include/fvattn.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^;(]*?\b(fvattn_\w+)\s*\(", text, re.M)))
+
+
+def status_string(status: int) -> str:
+    return load_library().fvattn_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise FvattnError(fn, status, status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t=None):
+    dev = t.device if t is not None else torch.device("cuda", torch.cuda.current_device())
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous on the GPU")
+
+
+def hilbert_permute(T: int, Y: int, X: int, perm: torch.Tensor, inv_perm: torch.Tensor):
+    _dev(perm, inv_perm)
+    _need(perm.dtype == torch.int32 and inv_perm.dtype == torch.int32, "int32 outputs")
+    _need(perm.numel() == T * Y * X == inv_perm.numel(), "outputs must hold T*Y*X")
+    _check("fvattn_hilbert_permute", load_library().fvattn_hilbert_permute(
+        T, Y, X, _ptr(perm), _ptr(inv_perm), _stream(perm)))
+
+
+def permute_rows(src: torch.Tensor, dst: torch.Tensor, index: torch.Tensor):
+    _dev(src, dst, index)
+    _need(src.dim() == 3 and src.shape == dst.shape and src.dtype == dst.dtype,
+          "src/dst must be [heads, n, d] of one dtype")
+    _need(index.dtype == torch.int32 and index.numel() == src.shape[1], "index int32[n]")
+    H, n, d = src.shape
+    _check("fvattn_permute_rows", load_library().fvattn_permute_rows(
+        _ptr(src), _ptr(dst), _ptr(index), H, n, d, _dtype_code(src), _stream(src)))
+
+
+def route_workspace_size(heads: int, n: int, d: int, block: int) -> int:
+    return int(load_library().fvattn_route_workspace_size(heads, n, d, block))
+
+
+def route(q, k, block: int, p: float, k_floor: int, mask, kv_count, kv_index,
+          head_load, head_density, workspace):
+    _dev(q, k, mask, kv_count, kv_index, head_load, head_density, workspace)
+    _need(q.shape == k.shape and q.dim() == 3 and q.dtype == k.dtype, "q, k [H, n, d]")
+    H, n, d = q.shape
+    nb = (n + block - 1) // block
+    _need(mask.dtype == torch.uint8 and mask.numel() == H * nb * nb, "mask u8[H,nB,nB]")
+    _need(kv_count.dtype == torch.int32 and kv_count.numel() == H * nb, "kv_count")
+    _need(kv_index.dtype == torch.int32 and kv_index.numel() == H * nb * nb, "kv_index")
+    _need(head_load.dtype == torch.int64 and head_load.numel() == H, "head_load")
+    _need(head_density.dtype == torch.float32 and head_density.numel() == H,
+          "head_density")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("fvattn_route", load_library().fvattn_route(
+        _ptr(q), _ptr(k), _dtype_code(q), H, n, d, block, float(p), int(k_floor),
+        _ptr(mask), _ptr(kv_count), _ptr(kv_index), _ptr(head_load),
+        _ptr(head_density), _ptr(workspace), ws_bytes, _stream(q)))
+
+
+def schedule_workspace_size(heads: int, n_qblocks: int, n_workers: int) -> int:
+    return int(load_library().fvattn_schedule_workspace_size(heads, n_qblocks, n_workers))
+
+
+def schedule(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
+             worker_load, workspace):
+    _dev(kv_count, lpt_order, worker_offsets, worker_tiles, worker_load, workspace)
+    _need(kv_count.dim() == 2 and kv_count.dtype == torch.int32, "kv_count i32[H, nB]")
+    H, nb = kv_count.shape
+    tiles = H * nb
+    _need(lpt_order.numel() == tiles and worker_tiles.numel() == tiles, "tile arrays")
+    _need(worker_offsets.numel() == n_workers + 1, "worker_offsets[W+1]")
+    _need(worker_load.numel() == n_workers and worker_load.dtype == torch.int64,
+          "worker_load i64[W]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("fvattn_schedule", load_library().fvattn_schedule(
+        _ptr(kv_count), H, nb, int(n_workers), _ptr(lpt_order), _ptr(worker_offsets),
+        _ptr(worker_tiles), _ptr(worker_load), _ptr(workspace), ws_bytes,
+        _stream(kv_count)))
+
+
+def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
+                worker_tiles=None, n_workers: int = 0, timing=None, scale: float = 0.0):
+    _dev(q, k, v, o, kv_count, kv_index)
+    _need(q.shape == k.shape == v.shape == o.shape and q.dim() == 3, "q,k,v,o [H, n, d]")
+    _need(q.dtype == k.dtype == v.dtype == o.dtype, "one dtype")
+    H, n, d = q.shape
+    nb = (n + block - 1) // block
+    _need(kv_count.numel() == H * nb and kv_index.numel() == H * nb * nb, "kv lists")
+    if worker_offsets is not None:
+        _dev(worker_offsets, worker_tiles)
+        _need(worker_offsets.numel() == n_workers + 1, "worker_offsets[W+1]")
+    if timing is not None:
+        _dev(timing)
+        _need(timing.numel() == 4 * n_workers and timing.element_size() == 8,
+              "timing u64[W][4]")
+    _check("fvattn_sparse_attn", load_library().fvattn_sparse_attn(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), H, n, d, block,
+        float(scale), _ptr(kv_count), _ptr(kv_index), _ptr(worker_offsets),
+        _ptr(worker_tiles), int(n_workers), _ptr(timing), _stream(q)))

@@ -1,0 +1,144 @@
+// C ABI: argument validation and dispatch.  Declarations and the contract of
+// each entry point are in include/fvattn.h.  Validation happens on the host
+// before any HIP call, so every error path is reachable without a GPU.
+#include <math.h>
+
+#include "fvattn.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool dtype_ok(int dtype) { return dtype == FVATTN_F32 || dtype == FVATTN_BF16; }
+
+size_t elem_size(int dtype) { return dtype == FVATTN_F32 ? 4 : 2; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FVATTN_OK : FVATTN_ELAUNCH; }
+
+bool fits_int32(long long x) { return x >= 0 && x <= 0x7fffffffLL; }
+
+int64_t nblocks(int n, int block) { return ((int64_t)n + block - 1) / block; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fvattn_status_string(int status) {
+  switch (status) {
+    case FVATTN_OK: return "ok";
+    case FVATTN_EINVAL: return "invalid argument";
+    case FVATTN_EUNSUPPORTED: return "unsupported configuration";
+    case FVATTN_ELAUNCH: return "kernel launch failed";
+    case FVATTN_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int fvattn_version(void) { return kVersion; }
+
+int fvattn_hilbert_permute(int T, int Y, int X, int32_t* perm, int32_t* inv_perm,
+                           hipStream_t stream) {
+  if (!perm || !inv_perm) return FVATTN_EINVAL;
+  if (T < 1 || Y < 1 || X < 1 || T > 1024 || Y > 1024 || X > 1024)
+    return FVATTN_EINVAL;
+  if (!fits_int32((long long)T * Y * X)) return FVATTN_EINVAL;
+  return launch_status(fvattn::launch_hilbert(T, Y, X, perm, inv_perm, stream));
+}
+
+int fvattn_permute_rows(const void* src, void* dst, const int32_t* index, int heads,
+                        int n, int d, int dtype, hipStream_t stream) {
+  if (!src || !dst || !index) return FVATTN_EINVAL;
+  if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1) return FVATTN_EINVAL;
+  if (src == dst) return FVATTN_EINVAL;
+  if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
+  return launch_status(fvattn::launch_permute_rows(
+      src, dst, index, heads, n, (size_t)d * elem_size(dtype), stream));
+}
+
+size_t fvattn_route_workspace_size(int heads, int n, int d, int block) {
+  if (heads < 1 || n < 1 || d < 1 || block < 1) return 0;
+  return fvattn::route_workspace_bytes(heads, n, d, block);
+}
+
+int fvattn_route(const void* q, const void* k, int dtype, int heads, int n, int d,
+                 int block, float p, int k_floor, uint8_t* mask, int32_t* kv_count,
+                 int32_t* kv_index, int64_t* head_load, float* head_density,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !mask || !kv_count || !kv_index || !head_load || !head_density)
+    return FVATTN_EINVAL;
+  if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
+  if (!(p > 0.f) || isnan(p) || k_floor < 0) return FVATTN_EINVAL;
+  if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
+  const int64_t nb = nblocks(n, block);
+  if (d > 256 || (dtype == FVATTN_BF16 ? d % 8 : d % 4) != 0) return FVATTN_EUNSUPPORTED;
+  if (nb > 4096) return FVATTN_EUNSUPPORTED;
+  const size_t need = fvattn::route_workspace_bytes(heads, n, d, block);
+  if (!workspace || workspace_bytes < need) return FVATTN_EWORKSPACE;
+  const fvattn::RouteWorkspace ws = fvattn::route_carve(workspace, heads, n, d, block);
+  return launch_status(fvattn::launch_route(q, k, dtype == FVATTN_BF16, heads, n, d, block,
+                                            p, k_floor, mask, kv_count, kv_index,
+                                            head_load, head_density, ws, stream));
+}
+
+size_t fvattn_schedule_workspace_size(int heads, int n_qblocks, int n_workers) {
+  if (heads < 1 || n_qblocks < 1 || n_workers < 1) return 0;
+  return fvattn::schedule_workspace_bytes(heads, n_qblocks, n_workers);
+}
+
+int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks, int n_workers,
+                    int32_t* lpt_order, int32_t* worker_offsets, int32_t* worker_tiles,
+                    int64_t* worker_load, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  if (!kv_count || !lpt_order || !worker_offsets || !worker_tiles || !worker_load)
+    return FVATTN_EINVAL;
+  if (heads < 1 || n_qblocks < 1 || n_workers < 1) return FVATTN_EINVAL;
+  if (!fits_int32((long long)heads * n_qblocks)) return FVATTN_EINVAL;
+  if (n_workers > fvattn::kMaxWorkers) return FVATTN_EUNSUPPORTED;
+  const size_t need = fvattn::schedule_workspace_bytes(heads, n_qblocks, n_workers);
+  if (!workspace || workspace_bytes < need) return FVATTN_EWORKSPACE;
+  return launch_status(fvattn::launch_schedule(kv_count, heads * n_qblocks, n_workers,
+                                               lpt_order, worker_offsets, worker_tiles,
+                                               worker_load, workspace, stream));
+}
+
+int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int dtype,
+                       int heads, int n, int d, int block, float scale,
+                       const int32_t* kv_count, const int32_t* kv_index,
+                       const int32_t* worker_offsets, const int32_t* worker_tiles,
+                       int n_workers, uint64_t* timing, hipStream_t stream) {
+  if (!q || !k || !v || !o || !kv_count || !kv_index) return FVATTN_EINVAL;
+  if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
+  if (isnan(scale) || isinf(scale)) return FVATTN_EINVAL;
+  if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
+  const int64_t nb = nblocks(n, block);
+  if (!fits_int32((long long)heads * nb) || !fits_int32(nb * nb)) return FVATTN_EINVAL;
+  if (worker_offsets) {
+    if (!worker_tiles || n_workers < 1) return FVATTN_EINVAL;
+  }
+  const bool bf16 = dtype == FVATTN_BF16;
+  if (!fvattn::attn_has_mfma_instance(bf16, d, block) && (d > 128 || block > 256))
+    return FVATTN_EUNSUPPORTED;
+  if (timing && !worker_offsets) return FVATTN_EINVAL;
+  fvattn::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.heads = heads;
+  a.n = n;
+  a.d = d;
+  a.block = block;
+  a.nb = (int)nb;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  a.kv_count = kv_count;
+  a.kv_index = kv_index;
+  a.worker_offsets = worker_offsets;
+  a.worker_tiles = worker_tiles;
+  a.n_workers = worker_offsets ? n_workers : 0;
+  a.timing = timing;
+  return launch_status(fvattn::launch_sparse_attn(a, bf16, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,445 @@
+// Block-sparse attention over the kept key blocks.
+//
+// Source: sparse attention computes only the (query block, key block) pairs
+// the routing keeps (aixai.ru FVAttn post, "What is sparse attention in video
+// transformers"; arXiv abstract on the mlsanity.com index page).  For tile
+// (h, i): O_i = softmax(Q_i K_S^T * scale) V_S over the rows S of the kept
+// blocks, evaluated block by block with an online (running max / running
+// sum) softmax in fp32.
+//
+// Two kernels:
+//
+// attn_mfma_kernel<D, BLK>  bf16 storage, MFMA v_mfma_f32_32x32x16_bf16.
+//   A workgroup owns one query block of BLK rows with BLK/32 wavefronts; each
+//   wavefront owns 32 queries.  Everything is computed transposed,
+//       S^T[key][q] = K Q^T      (A = K rows from LDS, B = Q from registers)
+//       O^T[d][q]  += V^T P^T    (A = V^T rows from LDS, B = P from registers)
+//   so in both accumulators lane l holds query l%32: the row max and row sum
+//   need one exchange with lane l^32, the rescale is a per-lane scalar, and
+//   the S^T accumulator registers are already the B operand of the PV product
+//   (the 16-key chunks are taken in the order the accumulator layout gives;
+//   V^T is read from LDS in that same order).  K is staged in LDS row-major
+//   with an XOR swizzle of its 16-byte chunks, V transposed with an XOR
+//   swizzle of its 8-byte units, both conflict-free for the MFMA reads.
+//   The softmax runs in the exp2 domain with scale*log2(e) folded into one
+//   FMA per score; P is rounded to bf16 (round to nearest even) for the PV
+//   product.
+//
+// attn_simple_kernel<T, DMAX>  plain fp32 VALU reference kernel for every
+//   other shape (fp32 inputs, small head dims, odd block sizes): one thread
+//   per query row, K/V staged through LDS in chunks of 32 rows.
+//
+// Both run either persistently (workgroup w walks its LPT list) or as a
+// head-major grid (one workgroup per tile), and write per-workgroup
+// timestamps (s_memrealtime, 100 MHz) plus the HW_ID / XCC_ID registers.
+#include <math.h>
+
+#include "device_util.h"
+#include "internal.h"
+
+namespace fvattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// hardware register ids for s_getreg (gfx9.4+): HW_ID and XCC_ID, 32 bits
+constexpr int kGetregHwId = (31 << 11) | 4;
+constexpr int kGetregXccId = (31 << 11) | 20;
+
+__device__ inline void stamp_start(uint64_t& t0) {
+  t0 = __builtin_amdgcn_s_memrealtime();
+}
+
+__device__ inline void stamp_end(uint64_t* timing, int w, uint64_t t0) {
+  const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+  timing[4 * (size_t)w + 0] = t0;
+  timing[4 * (size_t)w + 1] = t1;
+  timing[4 * (size_t)w + 2] = (uint64_t)__builtin_amdgcn_s_getreg(kGetregHwId);
+  timing[4 * (size_t)w + 3] = (uint64_t)__builtin_amdgcn_s_getreg(kGetregXccId);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite or +-inf).
+__device__ inline uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <typename T>
+__device__ inline float load_elem(const T* p);
+template <>
+__device__ inline float load_elem<float>(const float* p) { return *p; }
+template <>
+__device__ inline float load_elem<bf16s>(const bf16s* p) {
+  return bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+}
+
+template <typename T>
+__device__ inline void store_elem(T* p, float v);
+template <>
+__device__ inline void store_elem<float>(float* p, float v) { *p = v; }
+template <>
+__device__ inline void store_elem<bf16s>(bf16s* p, float v) {
+  *reinterpret_cast<uint16_t*>(p) = (uint16_t)bf16_bits(v);
+}
+
+// ---------------------------------------------------------------------------
+// Plain fp32 kernel.
+// ---------------------------------------------------------------------------
+constexpr int kSimpleThreads = 256;
+constexpr int kSimpleChunk = 32;
+
+template <typename T, int DMAX, bool PERSIST>
+__global__ __launch_bounds__(kSimpleThreads) void attn_simple_kernel(AttnArgs a) {
+  __shared__ float Ks[kSimpleChunk][DMAX];
+  __shared__ float Vs[kSimpleChunk][DMAX];
+  const int tid = threadIdx.x;
+  const int n = a.n, d = a.d, blk = a.block, nb = a.nb;
+  const T* Q = static_cast<const T*>(a.q);
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+  T* O = static_cast<T*>(a.o);
+  uint64_t t0 = 0;
+  if (PERSIST && a.timing && tid == 0) stamp_start(t0);
+
+  int beg = blockIdx.x, end = blockIdx.x + 1;
+  if (PERSIST) {
+    beg = a.worker_offsets[blockIdx.x];
+    end = a.worker_offsets[blockIdx.x + 1];
+  }
+  for (int it = beg; it < end; ++it) {
+    const int tile = PERSIST ? a.worker_tiles[it] : it;
+    const int h = tile / nb, i = tile - (tile / nb) * nb;
+    const int r = i * blk + tid;
+    const bool active = tid < blk && r < n;
+    const size_t hb = (size_t)h * n;
+    float qv[DMAX], acc[DMAX];
+#pragma unroll
+    for (int c = 0; c < DMAX; ++c) {
+      qv[c] = (active && c < d) ? load_elem(Q + (hb + r) * d + c) * a.scale_log2 : 0.f;
+      acc[c] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    const int cnt = min(a.kv_count[(size_t)h * nb + i], nb);
+    const int32_t* idx = a.kv_index + ((size_t)h * nb + i) * nb;
+    for (int jj = 0; jj < cnt; ++jj) {
+      const int j = idx[jj];
+      if (j < 0 || j >= nb) continue;          // malformed list entry: skip
+      const int r0 = j * blk, r1 = min(n, r0 + blk);
+      for (int kc = r0; kc < r1; kc += kSimpleChunk) {
+        __syncthreads();
+        for (int e = tid; e < kSimpleChunk * DMAX; e += kSimpleThreads) {
+          const int kr = e / DMAX, c = e % DMAX;
+          const int row = kc + kr;
+          const bool ok = row < r1 && c < d;
+          Ks[kr][c] = ok ? load_elem(K + (hb + row) * d + c) : 0.f;
+          Vs[kr][c] = ok ? load_elem(V + (hb + row) * d + c) : 0.f;
+        }
+        __syncthreads();
+        if (active) {
+          const int rows = min(kSimpleChunk, r1 - kc);
+          for (int kr = 0; kr < rows; ++kr) {
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < DMAX; ++c) s = fmaf(qv[c], Ks[kr][c], s);
+            const float mn = fmaxf(m, s);
+            const float corr = mn == -INFINITY ? 1.f : exp2f(m - mn);
+            const float pr = mn == -INFINITY ? 0.f : exp2f(s - mn);
+            l = l * corr + pr;
+#pragma unroll
+            for (int c = 0; c < DMAX; ++c) acc[c] = fmaf(pr, Vs[kr][c], acc[c] * corr);
+            m = mn;
+          }
+        }
+      }
+    }
+    if (active) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int c = 0; c < DMAX; ++c)
+        if (c < d) store_elem(O + (hb + r) * d + c, acc[c] * inv);
+    }
+  }
+  if (PERSIST && a.timing) {
+    __syncthreads();
+    if (tid == 0) stamp_end(a.timing, blockIdx.x, t0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel.
+// ---------------------------------------------------------------------------
+template <int D, int BLK>
+struct MfmaShape {
+  static constexpr int kWaves = BLK / 32;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kChunksPerRow = D / 8;      // 16-byte chunks of a K row
+  static constexpr int kUnitsPerRow = BLK / 4;     // 8-byte units of a V^T row
+  static constexpr int kKChunksPerThread = BLK * kChunksPerRow / kThreads;
+  static constexpr int kVUnitsPerThread = (BLK / 4) * (D / 8) / kThreads;
+  static_assert(kKChunksPerThread * kThreads == BLK * kChunksPerRow, "K staging");
+  static_assert(kVUnitsPerThread * kThreads == (BLK / 4) * (D / 8), "V staging");
+};
+
+// byte offset of 16-byte chunk c of K row r
+template <int D>
+__device__ inline uint32_t k_off(int r, int c) {
+  constexpr int CPR = D / 8;
+  return (uint32_t)(r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
+}
+
+// byte offset of 8-byte unit u (keys 4u..4u+3) of V^T row dd
+template <int BLK>
+__device__ inline uint32_t v_off(int dd, int u) {
+  constexpr int UPR = BLK / 4;
+  return (uint32_t)(dd * (2 * BLK) + ((u ^ (dd & (UPR - 1))) << 3));
+}
+
+template <int D, int BLK, bool PERSIST>
+__global__ __launch_bounds__(2 * BLK) void attn_mfma_kernel(AttnArgs a) {
+  using S = MfmaShape<D, BLK>;
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[BLK * D * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t Vt[D * BLK * 2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;      // query within the wavefront's 32
+  const int g = lane >> 5;        // which half of the K dimension this lane feeds
+  const int n = a.n, nb = a.nb;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+  uint16_t* O = static_cast<uint16_t*>(a.o);
+  const float sl2 = a.scale_log2;
+
+  uint64_t t0 = 0;
+  if (PERSIST && a.timing && tid == 0) stamp_start(t0);
+
+  int beg = blockIdx.x, end = blockIdx.x + 1;
+  if (PERSIST) {
+    beg = a.worker_offsets[blockIdx.x];
+    end = a.worker_offsets[blockIdx.x + 1];
+  }
+  for (int it = beg; it < end; ++it) {
+    const int tile = PERSIST ? a.worker_tiles[it] : it;
+    const int h = tile / nb;
+    const int i = tile - h * nb;
+    const size_t hb = (size_t)h * n;
+    const int qrow = i * BLK + wave * 32 + col;
+    const bool qvalid = qrow < n;
+
+    // Q^T operand: lane (col, g) holds Q[qrow][16*kk + 8*g .. +7]
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (qvalid)
+        w = *reinterpret_cast<const u32x4*>(Q + (hb + qrow) * D + 16 * kk + 8 * g);
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+    f32x16 acc_o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc_o[dt][e] = 0.f;
+    float m_run = -INFINITY;   // running max, log2-scaled units
+    float l_run = 0.f;         // running sum over this lane's half of the keys
+
+    const int cnt = min(a.kv_count[(size_t)h * nb + i], nb);
+    const int32_t* idx = a.kv_index + ((size_t)h * nb + i) * nb;
+    for (int jj = 0; jj < cnt; ++jj) {
+      const int j = __builtin_amdgcn_readfirstlane(idx[jj]);
+      if (j < 0 || j >= nb) continue;          // malformed list entry: skip
+      const int r0 = j * BLK;
+      __syncthreads();
+      // stage K rows (swizzled 16-byte chunks)
+#pragma unroll
+      for (int e = 0; e < S::kKChunksPerThread; ++e) {
+        const int gidx = tid + e * S::kThreads;
+        const int r = gidx / S::kChunksPerRow;
+        const int c = gidx % S::kChunksPerRow;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (r0 + r < n) w = *reinterpret_cast<const u32x4*>(K + (hb + r0 + r) * D + 8 * c);
+        *reinterpret_cast<u32x4*>(Ks + k_off<D>(r, c)) = w;
+      }
+      // stage V transposed: a unit is 4 keys x 8 columns
+#pragma unroll
+      for (int e = 0; e < S::kVUnitsPerThread; ++e) {
+        const int gidx = tid + e * S::kThreads;
+        const int c8 = gidx % (D / 8);
+        const int kq = gidx / (D / 8);
+        u32x4 rows[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = r0 + 4 * kq + x;
+          rows[x] = u32x4{0u, 0u, 0u, 0u};
+          if (r < n) rows[x] = *reinterpret_cast<const u32x4*>(V + (hb + r) * D + 8 * c8);
+        }
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          const int wsel = dd >> 1;
+          const int sh = (dd & 1) * 16;
+          const uint32_t k0 = (rows[0][wsel] >> sh) & 0xffffu;
+          const uint32_t k1 = (rows[1][wsel] >> sh) & 0xffffu;
+          const uint32_t k2 = (rows[2][wsel] >> sh) & 0xffffu;
+          const uint32_t k3 = (rows[3][wsel] >> sh) & 0xffffu;
+          const u32x2 pk = {k0 | (k1 << 16), k2 | (k3 << 16)};
+          *reinterpret_cast<u32x2*>(Vt + v_off<BLK>(8 * c8 + dd, kq)) = pk;
+        }
+      }
+      __syncthreads();
+
+      // S^T = K Q^T: tile kt covers keys 32*kt .. 32*kt+31 of the block
+      f32x16 s[BLK / 32];
+#pragma unroll
+      for (int kt = 0; kt < BLK / 32; ++kt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(Ks + k_off<D>(32 * kt + col, 2 * kk + g));
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
+                                                          qf[kk], s[kt], 0, 0, 0);
+        }
+      }
+      // accumulator layout: s[kt][e] is key 32*kt + 8*(e/4) + 4*g + e%4
+      if (r0 + BLK > n) {
+#pragma unroll
+        for (int kt = 0; kt < BLK / 32; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = r0 + 32 * kt + 8 * (e >> 2) + 4 * g + (e & 3);
+            if (key >= n) s[kt][e] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < BLK / 32; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx * sl2);
+      // m_new stays -inf only if every score so far is masked
+      const bool none = m_new == -INFINITY;
+      const float alpha = none ? 1.f : exp2f(m_run - m_new);
+      const float m_sub = none ? 0.f : m_new;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc_o[dt][e] *= alpha;
+
+      // P = exp2(S * sl2 - m), rounded to bf16 in accumulator order
+      uint32_t pk[BLK / 32][8];
+#pragma unroll
+      for (int kt = 0; kt < BLK / 32; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const float p0 = exp2f(fmaf(s[kt][e], sl2, -m_sub));
+          const float p1 = exp2f(fmaf(s[kt][e + 1], sl2, -m_sub));
+          l_run += p0 + p1;
+          pk[kt][e >> 1] = pack_bf16x2(p0, p1);
+        }
+
+      // O^T += V^T P^T over 16-key chunks c; chunk c uses accumulator
+      // registers 8*(c%2) .. +7 of tile c/2 = keys 16c + 8*(e/4) + 4g + e%4.
+#pragma unroll
+      for (int c = 0; c < BLK / 16; ++c) {
+        const u32x4 pb = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1],
+                          pk[c >> 1][4 * (c & 1) + 2], pk[c >> 1][4 * (c & 1) + 3]};
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int dd = 32 * dt + col;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(Vt + v_off<BLK>(dd, 4 * c + g));
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(Vt + v_off<BLK>(dd, 4 * c + 2 + g));
+          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                              bop, acc_o[dt], 0, 0, 0);
+        }
+      }
+    }
+
+    // normalise and store: acc_o[dt][e] is column d = 32dt + 8(e/4) + 4g + e%4
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qvalid) {
+      uint16_t* orow = O + (hb + qrow) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = 32 * dt + 8 * r4 + 4 * g;
+          const u32x2 w = {pack_bf16x2(acc_o[dt][4 * r4 + 0] * inv, acc_o[dt][4 * r4 + 1] * inv),
+                           pack_bf16x2(acc_o[dt][4 * r4 + 2] * inv, acc_o[dt][4 * r4 + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = w;
+        }
+    }
+  }
+  if (PERSIST && a.timing) {
+    __syncthreads();
+    if (tid == 0) stamp_end(a.timing, blockIdx.x, t0);
+  }
+}
+
+template <int D, int BLK>
+hipError_t launch_mfma(const AttnArgs& a, hipStream_t s) {
+  using S = MfmaShape<D, BLK>;
+  if (a.worker_offsets) {
+    hipLaunchKernelGGL((attn_mfma_kernel<D, BLK, true>), dim3(a.n_workers),
+                       dim3(S::kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_mfma_kernel<D, BLK, false>), dim3(a.heads * a.nb),
+                       dim3(S::kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int DMAX>
+hipError_t launch_simple(const AttnArgs& a, hipStream_t s) {
+  if (a.worker_offsets) {
+    hipLaunchKernelGGL((attn_simple_kernel<T, DMAX, true>), dim3(a.n_workers),
+                       dim3(kSimpleThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_simple_kernel<T, DMAX, false>), dim3(a.heads * a.nb),
+                       dim3(kSimpleThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_simple_any(const AttnArgs& a, hipStream_t s) {
+  if (a.d <= 32) return launch_simple<T, 32>(a, s);
+  if (a.d <= 64) return launch_simple<T, 64>(a, s);
+  return launch_simple<T, 128>(a, s);
+}
+
+}  // namespace
+
+bool attn_has_mfma_instance(bool bf16, int d, int block) {
+  if (!bf16) return false;
+  return (d == 64 || d == 128) && (block == 64 || block == 128);
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& a, bool bf16, hipStream_t s) {
+  if (attn_has_mfma_instance(bf16, a.d, a.block)) {
+    if (a.d == 128 && a.block == 128) return launch_mfma<128, 128>(a, s);
+    if (a.d == 64 && a.block == 64) return launch_mfma<64, 64>(a, s);
+    if (a.d == 64 && a.block == 128) return launch_mfma<64, 128>(a, s);
+    return launch_mfma<128, 64>(a, s);
+  }
+  if (bf16) return launch_simple_any<bf16s>(a, s);
+  return launch_simple_any<float>(a, s);
+}
+
+}  // namespace fvattn

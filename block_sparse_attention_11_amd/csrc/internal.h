@@ -1,0 +1,67 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernel files.
+// Every launcher only enqueues work on `stream` and returns the HIP status of
+// the launch; argument validation has already happened in abi.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fvattn {
+
+// bf16 storage element (bit pattern only; arithmetic is done in fp32).
+struct bf16s {
+  uint16_t bits;
+};
+
+// ---- hilbert.hip -----------------------------------------------------------
+hipError_t launch_hilbert(int T, int Y, int X, int32_t* perm, int32_t* inv,
+                          hipStream_t s);
+
+// ---- permute.hip -----------------------------------------------------------
+hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* index,
+                               int heads, int n, size_t row_bytes,
+                               hipStream_t s);
+
+// ---- route.hip -------------------------------------------------------------
+struct RouteWorkspace {
+  float* qbar;   // [heads][nB][d]
+  float* kbar;   // [heads][nB][d]
+  float* z;      // [heads][nB][nB]
+};
+size_t route_workspace_bytes(int heads, int n, int d, int block);
+RouteWorkspace route_carve(void* ws, int heads, int n, int d, int block);
+hipError_t launch_route(const void* q, const void* k, bool bf16, int heads,
+                        int n, int d, int block, float p, int k_floor,
+                        uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
+                        int64_t* head_load, float* head_density,
+                        const RouteWorkspace& ws, hipStream_t s);
+
+// ---- schedule.hip ----------------------------------------------------------
+constexpr int kMaxWorkers = 1024;
+constexpr int kMaxCost = 16383;
+size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers);
+hipError_t launch_schedule(const int32_t* kv_count, int tiles, int n_workers,
+                           int32_t* lpt_order, int32_t* worker_offsets,
+                           int32_t* worker_tiles, int64_t* worker_load,
+                           void* ws, hipStream_t s);
+
+// ---- attn.hip --------------------------------------------------------------
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int heads, n, d, block, nb;
+  float scale_log2;               // softmax scale * log2(e)
+  const int32_t* kv_count;        // [heads][nb]
+  const int32_t* kv_index;        // [heads][nb][nb]
+  const int32_t* worker_offsets;  // null => head-major grid launch
+  const int32_t* worker_tiles;
+  int n_workers;
+  uint64_t* timing;               // null or [n_workers][4]
+};
+bool attn_has_mfma_instance(bool bf16, int d, int block);
+hipError_t launch_sparse_attn(const AttnArgs& a, bool bf16, hipStream_t s);
+
+}  // namespace fvattn

@@ -1,0 +1,336 @@
+// Routing: block importance from mean-pooled Q/K, Top-p cut with a Top-k
+// floor, block mask, kept-block lists, per-head load and density.
+//
+// Sources: key-block importance is estimated from pooled Q and K, and one
+// routing pass gives the mask and the per-head density (PaperDaily FVAttn
+// article, method section; aixai.ru FVAttn post, "Sparse-routing frontend");
+// Top-p keeps blocks in importance order until the accumulated importance
+// reaches p (aixai.ru post, "Top-p vs Top-k"); the Top-k floor keeps at least
+// the k most important blocks (PaperDaily article, method section).
+// Readings: mean pooling over true rows, importance = softmax over key blocks
+// of qbar . kbar / sqrt(d), ranking by (importance desc, index asc), cut at
+// the first prefix whose mass is >= p.
+//
+// Kernels (all fp32 arithmetic):
+//   pool_kernel    one workgroup per (block, head, tensor): coalesced 16-byte
+//                  row loads, per-lane column sums, LDS reduction.  HBM-bound:
+//                  reads Q and K exactly once.
+//   score_kernel   z = qbar kbar^T * scale per head, LDS-tiled 64x64 fp32.
+//   select_kernel  one workgroup per (query block, head): row softmax, bitonic
+//                  sort of (P, ~j) keys in LDS, workgroup prefix sum, cut,
+//                  mask row and ascending kept list via a flag scan.
+//   load_kernel    per-head sum of kv_count (exact int64) and density.
+#include <math.h>
+
+#include "device_util.h"
+#include "internal.h"
+
+namespace fvattn {
+namespace {
+
+constexpr int kPoolThreads = 256;
+constexpr int kSelectThreads = 256;
+constexpr int kScoreTile = 64;
+constexpr int kScoreK = 16;
+
+__device__ inline void load_vec(const float* p, float out[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
+
+__device__ inline void load_vec(const bf16s* p, float out[8]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <typename T>
+struct VecWidth { static constexpr int value = 16 / sizeof(T); };
+
+// blockIdx.x = key/query block j, blockIdx.y = head, blockIdx.z = 0 (Q) / 1 (K)
+template <typename T>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ qbar,
+    float* __restrict__ kbar, int n, int d, int block, int nb) {
+  constexpr int VE = VecWidth<T>::value;
+  __shared__ float red[kPoolThreads * VE];
+  const int j = blockIdx.x, h = blockIdx.y;
+  const T* src = (blockIdx.z == 0 ? q : k) + (size_t)h * n * d;
+  float* dst = (blockIdx.z == 0 ? qbar : kbar) + ((size_t)h * nb + j) * d;
+  const int r0 = j * block;
+  const int r1 = min(n, r0 + block);
+  const int lanes_per_row = d / VE;
+  const int rows_per_pass = kPoolThreads / lanes_per_row;
+  const int tid = threadIdx.x;
+  const int lane = tid % lanes_per_row;
+  const int rsub = tid / lanes_per_row;
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+  if (rsub < rows_per_pass) {
+    for (int r = r0 + rsub; r < r1; r += rows_per_pass) {
+      float x[VE];
+      load_vec(src + (size_t)r * d + lane * VE, x);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[e] += x[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VE; ++e) red[tid * VE + e] = acc[e];
+  __syncthreads();
+  // red[rsub * d + col] holds the partial sum of rows r = rsub (mod passes).
+  const int used = min(rows_per_pass, r1 - r0);
+  const float inv = 1.0f / (float)(r1 - r0);
+  for (int col = tid; col < d; col += kPoolThreads) {
+    float s = 0.f;
+    for (int rs = 0; rs < used; ++rs) s += red[rs * d + col];
+    dst[col] = s * inv;
+  }
+}
+
+// z[h][i][j] = scale * sum_c qbar[h][i][c] * kbar[h][j][c]
+__global__ __launch_bounds__(256) void score_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar,
+    float* __restrict__ z, int nb, int d, float scale) {
+  __shared__ float As[kScoreK][kScoreTile + 4];
+  __shared__ float Bs[kScoreK][kScoreTile + 4];
+  const int h = blockIdx.z;
+  const int i0 = blockIdx.y * kScoreTile, j0 = blockIdx.x * kScoreTile;
+  const float* A = qbar + (size_t)h * nb * d;
+  const float* B = kbar + (size_t)h * nb * d;
+  const int tid = threadIdx.x;
+  const int ti = tid / 16, tj = tid % 16;   // 4x4 outputs per thread
+  float acc[4][4] = {};
+  for (int c0 = 0; c0 < d; c0 += kScoreK) {
+    // 64 rows x 16 columns of each operand: 1024 values, 4 per thread.
+    for (int e = tid; e < kScoreTile * kScoreK; e += 256) {
+      const int r = e / kScoreK, c = e % kScoreK;
+      const int ar = i0 + r, br = j0 + r, cc = c0 + c;
+      As[c][r] = (ar < nb && cc < d) ? A[(size_t)ar * d + cc] : 0.f;
+      Bs[c][r] = (br < nb && cc < d) ? B[(size_t)br * d + cc] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kScoreK; ++c) {
+      float a[4], b[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) a[x] = As[c][ti * 4 + x];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) b[y] = Bs[c][tj * 4 + y];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int i = i0 + ti * 4 + x;
+    if (i >= nb) continue;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int j = j0 + tj * 4 + y;
+      if (j < nb) z[((size_t)h * nb + i) * nb + j] = acc[x][y] * scale;
+    }
+  }
+}
+
+// One workgroup per row (i = blockIdx.x, h = blockIdx.y).  Dynamic LDS:
+// np uint64 sort keys + np floats (prefix sums) + np ints (flags/positions),
+// np = next power of two >= nb.
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(
+    const float* __restrict__ z, int nb, int np, float p, int k_floor,
+    uint8_t* __restrict__ mask, int32_t* __restrict__ kv_count,
+    int32_t* __restrict__ kv_index) {
+  extern __shared__ uint64_t smem[];
+  uint64_t* keys = smem;
+  float* cum = reinterpret_cast<float*>(keys + np);
+  int32_t* flag = reinterpret_cast<int32_t*>(cum + np);
+  __shared__ float s_redf[kSelectThreads / kWave];
+  __shared__ int32_t s_redi[kSelectThreads / kWave];
+
+  const int i = blockIdx.x, h = blockIdx.y;
+  const size_t row = (size_t)h * nb + i;
+  const float* zr = z + row * nb;
+  const int tid = threadIdx.x;
+
+  // softmax over the row
+  float mx = -INFINITY;
+  for (int j = tid; j < nb; j += kSelectThreads) mx = fmaxf(mx, zr[j]);
+  mx = block_reduce<kSelectThreads>(mx, s_redf, [](float a, float b) { return fmaxf(a, b); });
+  float sum = 0.f;
+  for (int j = tid; j < nb; j += kSelectThreads) {
+    const float e = expf(zr[j] - mx);
+    cum[j] = e;
+    sum += e;
+  }
+  // deterministic order: per-thread strided partials, then a fixed tree
+  sum = block_reduce<kSelectThreads>(sum, s_redf, [](float a, float b) { return a + b; });
+  for (int j = tid; j < np; j += kSelectThreads) {
+    if (j < nb) {
+      const float pj = cum[j] / sum;
+      keys[j] = ((uint64_t)__float_as_uint(pj) << 32) | (uint64_t)(~(uint32_t)j);
+    } else {
+      keys[j] = 0;                   // sorts after every real key
+    }
+  }
+  __syncthreads();
+
+  // bitonic sort, descending
+  for (int kk = 2; kk <= np; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int x = tid; x < np; x += kSelectThreads) {
+        const int y = x ^ jj;
+        if (y > x) {
+          const uint64_t a = keys[x], b = keys[y];
+          const bool desc = (x & kk) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            keys[x] = b;
+            keys[y] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // inclusive prefix sum of P in ranked order: contiguous per-thread chunks
+  const int per = np / kSelectThreads > 0 ? np / kSelectThreads : 1;
+  const int c0 = tid * per;
+  float run = 0.f;
+  for (int e = 0; e < per; ++e) {
+    const int x = c0 + e;
+    if (x < np) {
+      run += __uint_as_float((uint32_t)(keys[x] >> 32));
+      cum[x] = run;
+    }
+  }
+  __syncthreads();
+  {
+    // exclusive scan of the chunk totals (float, fixed order)
+    float* tot = reinterpret_cast<float*>(flag);   // reuse as scratch
+    tot[tid] = run;
+    __syncthreads();
+    float base = 0.f;
+    for (int t = 0; t < tid; ++t) base += tot[t];
+    __syncthreads();
+    for (int e = 0; e < per; ++e) {
+      const int x = c0 + e;
+      if (x < np) cum[x] += base;
+    }
+  }
+  __syncthreads();
+
+  int n_p = nb;
+  if (p < 1.0f) {
+    int first = nb;
+    for (int x = tid; x < nb; x += kSelectThreads)
+      if (cum[x] >= p) { first = min(first, x); }
+    first = block_reduce<kSelectThreads>(first, s_redi, [](int a, int b) { return min(a, b); });
+    n_p = first < nb ? first + 1 : nb;
+  }
+  const int n_keep = min(nb, max(n_p, k_floor));
+
+  for (int j = tid; j < nb; j += kSelectThreads) flag[j] = 0;
+  __syncthreads();
+  for (int x = tid; x < n_keep; x += kSelectThreads)
+    flag[~(uint32_t)(keys[x] & 0xffffffffu)] = 1;
+  __syncthreads();
+
+  uint8_t* mrow = mask + row * nb;
+  for (int j = tid; j < nb; j += kSelectThreads) mrow[j] = (uint8_t)flag[j];
+  // ascending compaction: contiguous chunks of j per thread, workgroup scan
+  const int perj = (nb + kSelectThreads - 1) / kSelectThreads;
+  const int j0 = tid * perj;
+  int mine = 0;
+  for (int e = 0; e < perj; ++e) {
+    const int j = j0 + e;
+    if (j < nb) mine += flag[j];
+  }
+  int total;
+  int pos = block_exclusive_scan<kSelectThreads>(mine, s_redi, total);
+  int32_t* irow = kv_index + row * nb;
+  for (int e = 0; e < perj; ++e) {
+    const int j = j0 + e;
+    if (j < nb && flag[j]) irow[pos++] = j;
+  }
+  if (tid == 0) kv_count[row] = n_keep;
+}
+
+__global__ __launch_bounds__(256) void load_kernel(
+    const int32_t* __restrict__ kv_count, int nb, int64_t* __restrict__ head_load,
+    float* __restrict__ head_density) {
+  __shared__ int64_t s_red[256 / kWave];
+  const int h = blockIdx.x;
+  int64_t s = 0;
+  for (int i = threadIdx.x; i < nb; i += 256) s += kv_count[(size_t)h * nb + i];
+  s = block_reduce<256>(s, s_red, [](int64_t a, int64_t b) { return a + b; });
+  if (threadIdx.x == 0) {
+    head_load[h] = s;
+    head_density[h] = (float)((double)s / ((double)nb * (double)nb));
+  }
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+size_t route_workspace_bytes(int heads, int n, int d, int block) {
+  const size_t nb = ((size_t)n + block - 1) / block;
+  const size_t pooled = align_up(sizeof(float) * (size_t)heads * nb * d, 256);
+  const size_t scores = align_up(sizeof(float) * (size_t)heads * nb * nb, 256);
+  return 2 * pooled + scores;
+}
+
+RouteWorkspace route_carve(void* ws, int heads, int n, int d, int block) {
+  const size_t nb = ((size_t)n + block - 1) / block;
+  const size_t pooled = align_up(sizeof(float) * (size_t)heads * nb * d, 256);
+  char* base = static_cast<char*>(ws);
+  RouteWorkspace w;
+  w.qbar = reinterpret_cast<float*>(base);
+  w.kbar = reinterpret_cast<float*>(base + pooled);
+  w.z = reinterpret_cast<float*>(base + 2 * pooled);
+  return w;
+}
+
+hipError_t launch_route(const void* q, const void* k, bool bf16, int heads,
+                        int n, int d, int block, float p, int k_floor,
+                        uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
+                        int64_t* head_load, float* head_density,
+                        const RouteWorkspace& ws, hipStream_t s) {
+  const int nb = (n + block - 1) / block;
+  if (bf16) {
+    hipLaunchKernelGGL(pool_kernel<bf16s>, dim3(nb, heads, 2),
+                       dim3(kPoolThreads), 0, s, (const bf16s*)q,
+                       (const bf16s*)k, ws.qbar, ws.kbar, n, d, block, nb);
+  } else {
+    hipLaunchKernelGGL(pool_kernel<float>, dim3(nb, heads, 2), dim3(kPoolThreads),
+                       0, s, (const float*)q, (const float*)k, ws.qbar, ws.kbar, n,
+                       d, block, nb);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned tiles = (unsigned)((nb + kScoreTile - 1) / kScoreTile);
+  hipLaunchKernelGGL(score_kernel, dim3(tiles, tiles, heads), dim3(256), 0, s,
+                     ws.qbar, ws.kbar, ws.z, nb, d, 1.0f / sqrtf((float)d));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int np = 1;
+  while (np < nb) np <<= 1;
+  if (np < kSelectThreads) np = kSelectThreads;
+  const size_t lds = (size_t)np * (sizeof(uint64_t) + sizeof(float) + sizeof(int32_t));
+  hipLaunchKernelGGL(select_kernel, dim3(nb, heads), dim3(kSelectThreads), lds, s,
+                     ws.z, nb, np, p, k_floor, mask, kv_count, kv_index);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(load_kernel, dim3(heads), dim3(256), 0, s, kv_count, nb,
+                     head_load, head_density);
+  return hipGetLastError();
+}
+
+}  // namespace fvattn

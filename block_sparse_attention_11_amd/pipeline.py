@@ -1,0 +1,104 @@
+"""The whole hot path for one grid shape, with its buffers.
+
+Allocation and call order only; each step is one C-ABI call into the HIP
+library:
+
+    hilbert_permute  (once per grid shape)
+    permute_rows     Q, K, V -> Hilbert order
+    route            pooled-Q/K Top-p + Top-k -> mask, kept lists, head load
+    schedule         LPT work list over (head, q-block) tiles
+    sparse_attn      persistent block-sparse attention over the kept blocks
+    permute_rows     O -> token order
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+def default_workers(device=None) -> int:
+    """One persistent workgroup per compute unit."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    return torch.cuda.get_device_properties(dev).multi_processor_count
+
+
+class FVAttnPath:
+    def __init__(self, heads: int, grid, d: int, block: int, dtype=torch.bfloat16,
+                 n_workers: int | None = None, device="cuda"):
+        self.heads, self.grid, self.d, self.block = heads, tuple(grid), d, block
+        T, Y, X = self.grid
+        self.n = T * Y * X
+        self.nb = (self.n + block - 1) // block
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.n_workers = n_workers or default_workers(self.device)
+        H, n, nb, dev = heads, self.n, self.nb, self.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.perm = torch.empty(n, **i32)
+        self.inv_perm = torch.empty(n, **i32)
+        self.qh = torch.empty((H, n, d), dtype=dtype, device=dev)
+        self.kh = torch.empty_like(self.qh)
+        self.vh = torch.empty_like(self.qh)
+        self.oh = torch.empty_like(self.qh)
+        self.mask = torch.empty((H, nb, nb), dtype=torch.uint8, device=dev)
+        self.kv_count = torch.empty((H, nb), **i32)
+        self.kv_index = torch.empty((H, nb, nb), **i32)
+        self.head_load = torch.empty(H, dtype=torch.int64, device=dev)
+        self.head_density = torch.empty(H, dtype=torch.float32, device=dev)
+        self.route_ws = torch.empty(_lib.route_workspace_size(H, n, d, block),
+                                    dtype=torch.uint8, device=dev)
+        W = self.n_workers
+        self.lpt_order = torch.empty(H * nb, **i32)
+        self.worker_offsets = torch.empty(W + 1, **i32)
+        self.worker_tiles = torch.empty(H * nb, **i32)
+        self.worker_load = torch.empty(W, dtype=torch.int64, device=dev)
+        self.sched_ws = torch.empty(_lib.schedule_workspace_size(H, nb, W),
+                                    dtype=torch.uint8, device=dev)
+        self.timing = torch.zeros((W, 4), dtype=torch.int64, device=dev)
+        self.ordered = False
+
+    # -- steps -------------------------------------------------------------
+    def order(self):
+        _lib.hilbert_permute(*self.grid, self.perm, self.inv_perm)
+        self.ordered = True
+
+    def to_hilbert(self, q, k, v):
+        _lib.permute_rows(q, self.qh, self.perm)
+        _lib.permute_rows(k, self.kh, self.perm)
+        _lib.permute_rows(v, self.vh, self.perm)
+
+    def route(self, p: float, k_floor: int):
+        _lib.route(self.qh, self.kh, self.block, p, k_floor, self.mask, self.kv_count,
+                   self.kv_index, self.head_load, self.head_density, self.route_ws)
+
+    def schedule(self):
+        _lib.schedule(self.kv_count, self.n_workers, self.lpt_order, self.worker_offsets,
+                      self.worker_tiles, self.worker_load, self.sched_ws)
+
+    def attend(self, balanced: bool = True, timing: bool = True):
+        if balanced:
+            _lib.sparse_attn(self.qh, self.kh, self.vh, self.oh, self.block,
+                             self.kv_count, self.kv_index, self.worker_offsets,
+                             self.worker_tiles, self.n_workers,
+                             self.timing if timing else None)
+        else:
+            _lib.sparse_attn(self.qh, self.kh, self.vh, self.oh, self.block,
+                             self.kv_count, self.kv_index)
+
+    def to_tokens(self, out):
+        _lib.permute_rows(self.oh, out, self.inv_perm)
+
+    def run(self, q, k, v, p: float, k_floor: int, out=None, balanced: bool = True):
+        """One pass of the whole path; returns O in token order."""
+        if out is None:
+            out = torch.empty_like(q)
+        if not self.ordered:
+            self.order()
+        self.to_hilbert(q, k, v)
+        self.route(p, k_floor)
+        self.schedule()
+        self.attend(balanced)
+        self.to_tokens(out)
+        return out

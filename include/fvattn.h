@@ -1,0 +1,191 @@
+/*
+ * fvattn.h - C ABI of the MI355X (gfx950) FVAttn single-GPU hot path.
+ *
+ * The method (FVAttn, "Adaptive Sparse Attention with Runtime Load Balancing
+ * for Video Generation"; arXiv abstract on the mlsanity.com index page):
+ * order the spatio-temporal token grid along a Hilbert curve, route each query
+ * block to the key blocks that matter with a Top-p threshold and a Top-k
+ * floor computed from pooled Q/K, and run attention over the kept blocks only.
+ * The pages balance the resulting uneven per-head work across GPU ranks; this
+ * library balances it across the workgroups of one GPU with an LPT work list
+ * that feeds a persistent attention kernel.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors Q, K, V, O are contiguous row-major [heads][n][d] in device
+ *    memory; a batch (or guidance copy) is folded into `heads`.
+ *  - Blocks: block j holds rows [j*block, min(n, (j+1)*block)); the last one
+ *    may be short.  nB = ceil(n / block).  Tile t = h * nB + i is query
+ *    block i of head h.
+ *  - dtype: FVATTN_F32 (float) or FVATTN_BF16 (bfloat16 storage, fp32
+ *    accumulation).
+ *  - Ownership: the caller allocates every buffer (outputs and workspace) and
+ *    keeps it alive until the stream work is done.  The library never
+ *    allocates, frees or caches device memory and keeps no global state; it
+ *    is re-entrant.
+ *  - Streams: every call only enqueues kernels on `stream` (0 = the null
+ *    stream) and returns; it never synchronises the host.
+ *  - Errors: arguments are validated on the host before anything is
+ *    launched; a failed check returns a negative status and launches nothing.
+ *    A failed launch returns FVATTN_ELAUNCH.  Faults inside a kernel surface
+ *    at the caller's next synchronisation.
+ */
+#ifndef FVATTN_H
+#define FVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define FVATTN_OK 0
+#define FVATTN_EINVAL (-1)       /* bad pointer, size or parameter            */
+#define FVATTN_EUNSUPPORTED (-2) /* valid, but no kernel instance for it     */
+#define FVATTN_ELAUNCH (-3)      /* the HIP launch itself failed             */
+#define FVATTN_EWORKSPACE (-4)   /* workspace pointer null or too small      */
+
+/* Storage types. */
+#define FVATTN_F32 0
+#define FVATTN_BF16 1
+
+/* Static string naming a status code. */
+const char* fvattn_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fvattn_version(void);
+
+/*
+ * Hilbert order of a T x Y x X token grid.
+ *
+ * Source: the routing frontend regroups tokens along a Hilbert curve so that
+ * spatially close tokens fall into the same or neighbouring blocks (aixai.ru
+ * FVAttn post, section "Sparse-routing frontend"; PaperDaily FVAttn article,
+ * method section).  Curve: J. Skilling's 3D construction on the enclosing
+ * cube of side 2^b, b = max(1, ceil(log2(max(T, Y, X)))), axis order (t, y, x),
+ * index bits interleaved MSB first with t on top; grid points are ranked by
+ * their index on that cube.
+ *
+ * Token n = (t*Y + y)*X + x.  Outputs (device, int32[T*Y*X] each):
+ *   perm[r]          = token at Hilbert rank r,
+ *   inv_perm[perm[r]] = r.
+ * Limits: 1 <= T, Y, X <= 1024 and T*Y*X < 2^31; otherwise FVATTN_EINVAL.
+ */
+int fvattn_hilbert_permute(int T, int Y, int X, int32_t* perm,
+                           int32_t* inv_perm, hipStream_t stream);
+
+/*
+ * Row gather, used to put Q/K/V into Hilbert order and O back:
+ *   dst[h][r][:] = src[h][index[r]][:]   for h < heads, r < n.
+ * index: device int32[n], every entry in [0, n) (not checked on the device).
+ * src and dst must not overlap.  d >= 1.
+ */
+int fvattn_permute_rows(const void* src, void* dst, const int32_t* index,
+                        int heads, int n, int d, int dtype,
+                        hipStream_t stream);
+
+/*
+ * Routing: block importance from mean-pooled Q/K, Top-p cut, Top-k floor.
+ *
+ * Source: importance of key blocks is estimated from pooled Q and K, and one
+ * routing pass yields the mask and each head's density (PaperDaily FVAttn
+ * article, method section; aixai.ru post, "Sparse-routing frontend"); Top-p
+ * keeps blocks in importance order until their accumulated importance
+ * reaches p (aixai.ru post, "Top-p vs Top-k"); the Top-k floor always keeps
+ * the k most important ones (PaperDaily article, method section).
+ *
+ * Computed, on Hilbert-ordered q, k [heads][n][d]:
+ *   qbar[h][i] = mean of q rows of block i (true row count), same for kbar;
+ *   z[h][i][j] = qbar[h][i] . kbar[h][j] / sqrt(d);
+ *   P[h][i][:] = softmax_j z[h][i][:];
+ *   blocks ranked by (P descending, j ascending); n_p = smallest prefix whose
+ *   accumulated P is >= p (nB if p >= 1 or if none reaches p);
+ *   n_keep = min(nB, max(n_p, k_floor)).
+ * Outputs (device):
+ *   mask        uint8 [heads][nB][nB], 1 = kept;
+ *   kv_count    int32 [heads][nB] = n_keep;
+ *   kv_index    int32 [heads][nB][nB], kept j ascending in the first
+ *               kv_count entries of each row (the rest is left untouched);
+ *   head_load   int64 [heads] = sum_i kv_count[h][i];
+ *   head_density float [heads] = head_load / nB^2.
+ * Arithmetic is fp32 on the device (pooling, scores, softmax, prefix sums).
+ * Limits: d <= 256 and d % 8 == 0 (bf16) or d % 4 == 0 (f32); nB <= 4096;
+ * 0 < p (p >= 1 keeps everything); k_floor >= 0.
+ * workspace: device memory of at least fvattn_route_workspace_size() bytes.
+ */
+size_t fvattn_route_workspace_size(int heads, int n, int d, int block);
+int fvattn_route(const void* q, const void* k, int dtype, int heads, int n,
+                 int d, int block, float p, int k_floor, uint8_t* mask,
+                 int32_t* kv_count, int32_t* kv_index, int64_t* head_load,
+                 float* head_density, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/*
+ * LPT work list over (head, q-block) tiles for n_workers persistent
+ * workgroups.
+ *
+ * Source: once the mask exists each head's load in sparse blocks is known
+ * exactly and a few heavy heads set the critical path (aixai.ru FVAttn post,
+ * section "Runtime Load Balancing (RLB)").  On one GPU the balanced resource
+ * is the set of workgroups; the rule is Graham's LPT:
+ *   cost(t) = kv_count[t] (t = h*n_qblocks + i);
+ *   lpt_order = tiles sorted by (cost descending, t ascending);
+ *   in that order each tile goes to the worker with the least load so far
+ *   (lowest worker index on ties) and is appended to its list.
+ * Outputs (device):
+ *   lpt_order      int32 [heads*n_qblocks];
+ *   worker_offsets int32 [n_workers+1], exclusive prefix of list sizes;
+ *   worker_tiles   int32 [heads*n_qblocks], the lists concatenated;
+ *   worker_load    int64 [n_workers], summed cost per worker.
+ * Bit-exact: there is exactly one correct result per input.
+ * Limits: 1 <= n_workers <= 1024; costs in [0, 65535]; heads*n_qblocks < 2^31.
+ * workspace: at least fvattn_schedule_workspace_size() bytes.
+ */
+size_t fvattn_schedule_workspace_size(int heads, int n_qblocks, int n_workers);
+int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
+                    int n_workers, int32_t* lpt_order, int32_t* worker_offsets,
+                    int32_t* worker_tiles, int64_t* worker_load,
+                    void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * Block-sparse attention over the kept blocks.
+ *
+ * Source: only the (query block, key block) pairs the routing keeps are
+ * computed (aixai.ru FVAttn post, "What is sparse attention in video
+ * transformers"; arXiv abstract).  For each tile (h, i):
+ *   O[h][rows of block i] = softmax(Q_i K_S^T * scale) V_S,
+ * S = the rows of the blocks kv_index[h][i][0 .. kv_count[h][i]).  No causal
+ * mask.  fp32 accumulation; O is stored in dtype.  A row with kv_count 0 is
+ * written as zeros.
+ *
+ * scale <= 0 selects 1/sqrt(d).
+ * Work distribution:
+ *   worker_offsets != NULL: persistent launch of n_workers workgroups;
+ *     workgroup w runs the tiles worker_tiles[worker_offsets[w] ..
+ *     worker_offsets[w+1]) in order (the LPT lists of fvattn_schedule);
+ *   worker_offsets == NULL: one workgroup per tile in head-major order (the
+ *     unbalanced control); worker_tiles and n_workers are ignored.
+ * timing (nullable, device uint64 [n_workers][4], persistent launch only):
+ *   {start, end} of each workgroup on the 100 MHz constant clock
+ *   (s_memrealtime), the raw HW_ID register and the XCC_ID register.
+ * Kernels: bf16 with (d, block) in {(64, 64), (128, 128), (64, 128),
+ * (128, 64)} runs on the MFMA kernel; every other (dtype, d <= 128,
+ * block <= 256) combination runs on a plain fp32 VALU kernel.
+ */
+int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o,
+                       int dtype, int heads, int n, int d, int block,
+                       float scale, const int32_t* kv_count,
+                       const int32_t* kv_index, const int32_t* worker_offsets,
+                       const int32_t* worker_tiles, int n_workers,
+                       uint64_t* timing, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FVATTN_H */

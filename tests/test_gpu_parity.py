@@ -1,0 +1,333 @@
+"""GPU parity: every step of the HIP path against the CPU oracle, through the
+C ABI, on seeded synthetic inputs.
+
+Stage-wise on identical inputs: the oracle's LPT runs on the GPU's kv_count
+and the oracle's attention on the GPU's kept lists; Hilbert order and LPT
+must match bit for bit, masks per the row protocol in tests/parity.py, and
+attention within max-abs 2e-2 (bf16) / 1e-4 (fp32) plus a relative-L2 bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_11_amd import _lib, synth
+from block_sparse_attention_11_amd.pipeline import FVAttnPath
+from oracle import attention as oat
+from oracle import hilbert as ohb
+from oracle import lpt as olpt
+from oracle import route as ort
+from tests.parity import TOL, attn_errors, classify_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def to_np(t):
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.detach().cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Hilbert
+# ---------------------------------------------------------------------------
+GRIDS = [(1, 1, 1), (1, 1, 5), (2, 2, 2), (2, 8, 8), (3, 5, 7), (17, 1, 3),
+         (4, 16, 16), (16, 16, 16), (21, 30, 52), (21, 45, 80), (41, 45, 80),
+         (1, 300, 2), (33, 17, 65)]
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+def test_hilbert_bit_exact(grid):
+    say(f"hilbert {grid}")
+    n = grid[0] * grid[1] * grid[2]
+    perm = torch.full((n,), -7, dtype=torch.int32, device=DEV)
+    inv = torch.full((n,), -7, dtype=torch.int32, device=DEV)
+    _lib.hilbert_permute(*grid, perm, inv)
+    torch.cuda.synchronize()
+    rp, ri = ohb.hilbert_order(*grid)
+    assert np.array_equal(perm.cpu().numpy(), rp)
+    assert np.array_equal(inv.cpu().numpy(), ri)
+
+
+# ---------------------------------------------------------------------------
+# Permute
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64),
+                                     (torch.bfloat16, 6), (torch.float32, 3)])
+def test_permute_rows_bit_exact(dtype, d):
+    say(f"permute {dtype} d={d}")
+    g = torch.Generator().manual_seed(5)
+    H, n = 3, 1000
+    x = torch.randn((H, n, d), generator=g).to(dtype)
+    idx = torch.randperm(n, generator=g).to(torch.int32)
+    dst = torch.empty((H, n, d), dtype=dtype, device=DEV)
+    _lib.permute_rows(x.to(DEV), dst, idx.to(DEV))
+    ref = ort.permute_rows(x.view(torch.int16 if dtype == torch.bfloat16 else torch.int32)
+                           .numpy(), idx.numpy())
+    got = dst.cpu().view(torch.int16 if dtype == torch.bfloat16 else torch.int32).numpy()
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# Routing
+# ---------------------------------------------------------------------------
+def run_route(w, q, k, p, kf):
+    """GPU route on Hilbert-ordered inputs; returns numpy outputs + the
+    Hilbert-ordered float64 inputs for the oracle."""
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, n_workers=8, device=DEV)
+    path.order()
+    path.to_hilbert(q, k, k)
+    path.route(p, kf)
+    torch.cuda.synchronize()
+    return path
+
+
+ROUTE_CASES = [
+    ("tiny", None, None),
+    ("small", None, None),
+    ("small", 0.5, 1),
+    ("small", 1.0, 0),
+    ("small", 0.2, 20),      # floor beyond nB
+    ("ragged_f32", 0.6, 2),
+    ("ragged_bf16", 0.8, 3),
+    ("mid_bf16", 0.95, 8),
+]
+
+
+def workload(name):
+    W = synth.WORKLOADS
+    if name in W:
+        return W[name]
+    if name == "ragged_f32":
+        return synth.Workload("ragged_f32", 2, 32, (3, 5, 7), 16, 0.6, 2, "f32")
+    if name == "ragged_bf16":
+        return synth.Workload("ragged_bf16", 3, 64, (3, 5, 7), 16, 0.8, 3, "bf16",
+                              s_range=(1.0, 64.0))
+    if name == "mid_bf16":
+        # several 128-blocks with an 80-row tail, MFMA shape (d=128, block=128)
+        return synth.Workload("mid_bf16", 3, 128, (5, 9, 16), 128, 0.95, 8, "bf16",
+                              s_range=(4.0, 256.0))
+    if name == "mid_bf16_64":
+        return synth.Workload("mid_bf16_64", 2, 64, (3, 10, 13), 64, 0.9, 4, "bf16",
+                              s_range=(2.0, 128.0))
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name,p,kf", ROUTE_CASES)
+def test_route_parity(name, p, kf):
+    w = workload(name)
+    p = w.p if p is None else p
+    kf = w.k if kf is None else kf
+    say(f"route {name} p={p} k={kf}")
+    q, k, v, _ = synth.make_inputs(w, "cpu")
+    path = run_route(w, q.to(DEV), k.to(DEV), p, kf)
+    perm, _ = ohb.hilbert_order(*w.grid)
+    assert np.array_equal(path.perm.cpu().numpy(), perm)
+    qh = ort.permute_rows(to_np(q).astype(np.float64), perm)
+    kh = ort.permute_rows(to_np(k).astype(np.float64), perm)
+    # the GPU's Hilbert-ordered copies are the same bytes
+    assert np.array_equal(to_np(path.qh), qh.astype(to_np(path.qh).dtype))
+    ora = ort.route(qh, kh, w.block, p, kf)
+    ws = path.route_ws
+    nb, H, d = path.nb, w.heads, w.d
+    qbar = ws[:H * nb * d * 4].view(torch.float32).reshape(H, nb, d).cpu().numpy()
+    assert np.allclose(qbar, ora["qbar"], rtol=1e-5, atol=1e-6)
+    gc = path.kv_count.cpu().numpy()
+    gi = path.kv_index.cpu().numpy()
+    stats, bad = classify_rows(ora["P"], p, kf, gc, gi, ora["kv_count"], ora["kv_index"])
+    say(f"  mask rows {stats}")
+    assert stats["unexplained"] == 0, bad[:10]
+    gm = path.mask.cpu().numpy()
+    for h in range(H):
+        for i in range(nb):
+            assert np.flatnonzero(gm[h, i]).tolist() == gi[h, i, :gc[h, i]].tolist()
+    load = path.head_load.cpu().numpy()
+    assert np.array_equal(load, gc.astype(np.int64).sum(1))
+    dens = path.head_density.cpu().numpy()
+    assert np.array_equal(dens, (load / float(nb * nb)).astype(np.float32))
+    assert (gc >= min(kf, nb)).all()
+
+
+# ---------------------------------------------------------------------------
+# LPT schedule
+# ---------------------------------------------------------------------------
+def gpu_schedule(costs_2d, W):
+    H, nb = costs_2d.shape
+    kvc = torch.from_numpy(costs_2d.astype(np.int32)).to(DEV)
+    tiles = H * nb
+    order = torch.empty(tiles, dtype=torch.int32, device=DEV)
+    off = torch.empty(W + 1, dtype=torch.int32, device=DEV)
+    wt = torch.empty(tiles, dtype=torch.int32, device=DEV)
+    wl = torch.empty(W, dtype=torch.int64, device=DEV)
+    ws = torch.empty(_lib.schedule_workspace_size(H, nb, W), dtype=torch.uint8, device=DEV)
+    _lib.schedule(kvc, W, order, off, wt, wl, ws)
+    torch.cuda.synchronize()
+    return order.cpu().numpy(), off.cpu().numpy(), wt.cpu().numpy(), wl.cpu().numpy()
+
+
+SCHED_CASES = [
+    ("hand", np.array([[7, 5, 4, 3, 3, 2]]), 2),
+    ("one_worker", np.array([[4, 9, 1, 9, 0]]), 1),
+    ("more_workers", np.array([[2, 5, 5]]), 5),
+    ("all_zero", np.zeros((2, 7), dtype=np.int64), 3),
+    ("equal", np.full((40, 591), 561), 256),
+    ("random_ties", None, 64),
+    ("random_wide", None, 1024),
+    ("random_odd", None, 100),
+    ("big_costs", None, 256),
+]
+
+
+@pytest.mark.parametrize("name,costs,W", SCHED_CASES)
+def test_schedule_bit_exact(name, costs, W):
+    say(f"schedule {name} W={W}")
+    rng = np.random.default_rng(sum(map(ord, name)))
+    if name == "random_ties":
+        costs = rng.integers(1, 9, size=(8, 37))
+    elif name == "random_wide":
+        costs = rng.integers(0, 600, size=(40, 591))
+    elif name == "random_odd":
+        costs = rng.integers(8, 1155, size=(40, 1154))
+    elif name == "big_costs":
+        costs = rng.integers(0, 16384, size=(5, 333))
+    got = gpu_schedule(costs, W)
+    ref = olpt.lpt_schedule(costs.reshape(-1), W)
+    for g, r, what in zip(got, ref, ("order", "offsets", "tiles", "loads")):
+        assert np.array_equal(g, r), what
+
+
+# ---------------------------------------------------------------------------
+# Attention on the GPU's kept lists
+# ---------------------------------------------------------------------------
+ATTN_CASES = ["tiny", "small", "ragged_f32", "ragged_bf16", "mid_bf16", "mid_bf16_64"]
+
+
+@pytest.mark.parametrize("name", ATTN_CASES)
+@pytest.mark.parametrize("balanced", [True, False])
+def test_attention_parity(name, balanced):
+    w = workload(name)
+    say(f"attention {name} balanced={balanced}")
+    q, k, v, _ = synth.make_inputs(w, "cpu")
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, n_workers=7,
+                      device=DEV)
+    out = path.run(q.to(DEV), k.to(DEV), v.to(DEV), w.p, w.k, balanced=balanced)
+    torch.cuda.synchronize()
+    perm = path.perm.cpu().numpy()
+    qh, kh, vh = (ort.permute_rows(to_np(x).astype(np.float64), perm) for x in (q, k, v))
+    ref_h = oat.block_sparse_attention(qh, kh, vh, w.block, path.kv_count.cpu().numpy(),
+                                       path.kv_index.cpu().numpy())
+    ref = oat.unpermute_rows(ref_h, perm)
+    err = attn_errors(to_np(out), ref)
+    say(f"  {err}")
+    tol = TOL[w.dtype]
+    assert err["max_abs"] <= tol["max_abs"] and err["rel_l2"] <= tol["rel_l2"], err
+    # the Hilbert-ordered output agrees with the token-order one
+    assert np.array_equal(to_np(path.oh), ort.permute_rows(to_np(out), perm))
+
+
+@pytest.mark.parametrize("name", ["small", "mid_bf16", "ragged_f32"])
+def test_dense_control_matches_brute_force(name):
+    """p = 1 keeps every block: the path must equal plain dense attention in
+    the original token order."""
+    w = workload(name)
+    say(f"dense control {name}")
+    q, k, v, _ = synth.make_inputs(w, "cpu")
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, device=DEV)
+    out = path.run(q.to(DEV), k.to(DEV), v.to(DEV), 1.0, 0)
+    torch.cuda.synchronize()
+    assert (path.kv_count.cpu().numpy() == path.nb).all()
+    assert (path.head_density.cpu().numpy() == 1.0).all()
+    ref = oat.dense_attention(to_np(q), to_np(k), to_np(v))
+    err = attn_errors(to_np(out), ref)
+    say(f"  {err}")
+    tol = TOL[w.dtype]
+    assert err["max_abs"] <= tol["max_abs"] and err["rel_l2"] <= tol["rel_l2"], err
+
+
+@pytest.mark.parametrize("dtype,d,block", [(torch.bfloat16, 128, 128),
+                                           (torch.bfloat16, 64, 64),
+                                           (torch.float32, 64, 16)])
+def test_attention_handmade_lists(dtype, d, block):
+    """Edge cases: an empty row (written as zeros), a single kept block, only
+    the short tail block, and constant V rows."""
+    say(f"handmade lists {dtype} d={d} block={block}")
+    H, n = 2, 3 * block + block // 2 + 1
+    nb = 4
+    g = torch.Generator().manual_seed(3)
+    q = (torch.randn((H, n, d), generator=g) * 2).to(dtype)
+    k = (torch.randn((H, n, d), generator=g) * 2).to(dtype)
+    v = torch.randn((H, n, d), generator=g).to(dtype)
+    cnt = np.array([[0, 1, 1, 4], [2, 1, 3, 1]], dtype=np.int32)
+    idx = np.zeros((H, nb, nb), dtype=np.int32)
+    idx[0, 1, 0] = 3
+    idx[0, 2, 0] = 0
+    idx[0, 3, :4] = [0, 1, 2, 3]
+    idx[1, 0, :2] = [1, 3]
+    idx[1, 1, 0] = 1
+    idx[1, 2, :3] = [0, 2, 3]
+    idx[1, 3, 0] = 3
+    o = torch.full((H, n, d), float("nan"), dtype=dtype, device=DEV)
+    _lib.sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), o, block,
+                     torch.from_numpy(cnt).to(DEV), torch.from_numpy(idx).to(DEV))
+    torch.cuda.synchronize()
+    got = to_np(o)
+    qq, kk, vv = (to_np(x).astype(np.float64) for x in (q, k, v))
+    assert (got[0, :block] == 0).all()
+    tiles = [(h, i) for h in range(H) for i in range(nb) if cnt[h, i] > 0]
+    ref = oat.block_sparse_attention(qq, kk, vv, block, cnt, idx, tiles=tiles)
+    mask = ~np.isnan(ref)
+    err = attn_errors(got[mask], ref[mask])
+    tol = TOL["bf16" if dtype == torch.bfloat16 else "f32"]
+    assert err["max_abs"] <= tol["max_abs"] and err["rel_l2"] <= tol["rel_l2"], err
+    # constant V rows give the constant, whatever the mask
+    vc = torch.arange(d, dtype=torch.float32).div(d).expand(H, n, d).contiguous().to(dtype)
+    _lib.sparse_attn(q.to(DEV), k.to(DEV), vc.to(DEV), o, block,
+                     torch.from_numpy(cnt).to(DEV), torch.from_numpy(idx).to(DEV))
+    torch.cuda.synchronize()
+    got = to_np(o)
+    exp = to_np(vc)
+    for h, i in tiles:
+        r0, r1 = i * block, min(n, (i + 1) * block)
+        assert np.abs(got[h, r0:r1] - exp[h, r0:r1]).max() <= tol["max_abs"]
+
+
+def test_rerun_is_bitwise_deterministic():
+    w = workload("mid_bf16")
+    say("determinism mid_bf16")
+    q, k, v, _ = synth.make_inputs(w, "cpu")
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, device=DEV)
+    outs = []
+    for _ in range(2):
+        o = path.run(q, k, v, w.p, w.k)
+        torch.cuda.synchronize()
+        outs.append([x.clone() for x in (o, path.mask, path.kv_index, path.worker_tiles,
+                                         path.worker_offsets)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    # balanced and head-major launches run the same per-tile arithmetic
+    path.attend(balanced=False)
+    torch.cuda.synchronize()
+    o2 = torch.empty_like(q)
+    path.to_tokens(o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, outs[0][0])
+
+
+def test_timing_records_every_worker():
+    w = workload("mid_bf16")
+    say("timing mid_bf16")
+    q, k, v, _ = synth.make_inputs(w, "cpu")
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, n_workers=5, device=DEV)
+    path.run(q.to(DEV), k.to(DEV), v.to(DEV), w.p, w.k)
+    torch.cuda.synchronize()
+    t = path.timing.cpu().numpy().astype(np.uint64)
+    assert (t[:, 1] >= t[:, 0]).all() and (t[:, 0] > 0).all()
+    # every worker ran inside one kernel launch: the spans overlap
+    assert t[:, 0].max() <= t[:, 1].min() + 10_000_000
