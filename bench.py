@@ -1,0 +1,290 @@
+"""Benchmark of the FVAttn hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input that
+is already resident in HBM: Hilbert order, Q/K/V permute, routing (pooled
+Q/K, Top-p + Top-k), LPT schedule, persistent block-sparse attention, O
+permute back.
+
+Prints ONE JSON line.  `value` = kept-block FLOPs (sum over kept (h, i, j) of
+4 * n_i * n_j * d, true block sizes) per second of the whole step, in
+TFLOP/s.  The attention-only rate, the dense (p = 1) control and its
+speedup, the head-major (unbalanced) control, per-CU busy-time imbalance,
+the attention kernel's roofline and the CPU oracle baseline ride along.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_sparse_attention_11_amd import synth  # noqa: E402
+from block_sparse_attention_11_amd.pipeline import FVAttnPath  # noqa: E402
+
+METRIC = "effective TFLOP/s on kept blocks + speedup vs dense, 720p-shaped, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0           # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+ATTN_SOURCES = ["block_sparse_attention_11_amd/csrc/attn.hip",
+                "block_sparse_attention_11_amd/csrc/internal.h",
+                "block_sparse_attention_11_amd/csrc/device_util.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_720p_traffic.txt")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kept_flops(path: FVAttnPath) -> float:
+    """sum over kept (h, i, j) of 4 * n_i * n_j * d, in float64 on the GPU."""
+    nb, blk, n, d = path.nb, path.block, path.n, path.d
+    sizes = torch.full((nb,), blk, dtype=torch.float64, device=path.device)
+    sizes[-1] = n - (nb - 1) * blk
+    kept_rows = path.mask.to(torch.float64) @ sizes          # [H, nb]
+    return float((4.0 * d * kept_rows * sizes[None, :]).sum().item())
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counters, or
+    None when they are missing, for another workload, or the kernel changed."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    a, b = line.split(":", 1)
+                    kv[a.strip()] = b.strip()
+        if kv.get("workload") != workload or kv.get("attn_source_sha256") != source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cu_imbalance(timing: np.ndarray):
+    """Per-CU busy time from the persistent workgroups' timestamps."""
+    t = timing.astype(np.uint64)
+    start, end = t[:, 0].astype(np.float64), t[:, 1].astype(np.float64)
+    hw, xcc = t[:, 2], t[:, 3]
+    cu = (hw >> np.uint64(8)) & np.uint64(0xF)
+    sh = (hw >> np.uint64(12)) & np.uint64(1)
+    se = (hw >> np.uint64(13)) & np.uint64(7)
+    key = ((xcc & np.uint64(0xF)) << np.uint64(8)) | (se << np.uint64(5)) | (sh << np.uint64(4)) | cu
+    busy = {}
+    for k, s, e in zip(key.tolist(), start, end):
+        lo, hi = busy.get(k, (s, e))
+        busy[k] = (min(lo, s), max(hi, e))
+    spans = np.array([hi - lo for lo, hi in busy.values()]) / 100.0   # 100 MHz -> us
+    wg = (end - start) / 100.0
+    return {"cus": len(busy), "workgroups": int(t.shape[0]),
+            "cu_busy_us_max": float(spans.max()), "cu_busy_us_mean": float(spans.mean()),
+            "cu_busy_us_min": float(spans.min()),
+            "max_over_mean": float(spans.max() / spans.mean()),
+            "max_over_min": float(spans.max() / max(spans.min(), 1e-9)),
+            "wg_max_over_mean": float(wg.max() / wg.mean()),
+            "xcds": int(len(set((xcc & np.uint64(0xF)).tolist())))}
+
+
+class StageTimer:
+    """HIP events on the stream the library launches on (torch's current one)."""
+
+    def __init__(self):
+        self.ev = {}
+
+    def mark(self, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.ev.setdefault(name, []).append(e)
+
+    def durations(self, a, b):
+        return [x.elapsed_time(y) for x, y in zip(self.ev[a], self.ev[b])]
+
+
+def timed_step(path, q, k, v, out, p, kf, tm: StageTimer | None, balanced=True):
+    if tm: tm.mark("s0")
+    path.order()
+    if tm: tm.mark("s1")
+    path.to_hilbert(q, k, v)
+    if tm: tm.mark("s2")
+    path.route(p, kf)
+    if tm: tm.mark("s3")
+    path.schedule()
+    if tm: tm.mark("s4")
+    path.attend(balanced=balanced)
+    if tm: tm.mark("s5")
+    path.to_tokens(out)
+    if tm: tm.mark("s6")
+
+
+def run_steps(path, q, k, v, out, p, kf, steps, warmup, balanced=True):
+    for _ in range(warmup):
+        timed_step(path, q, k, v, out, p, kf, None, balanced)
+    torch.cuda.synchronize()
+    tm = StageTimer()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        timed_step(path, q, k, v, out, p, kf, tm, balanced)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    names = ["hilbert", "permute_in", "route", "schedule", "attention", "permute_out"]
+    stages = {nm: float(np.mean(tm.durations(f"s{i}", f"s{i + 1}")))
+              for i, nm in enumerate(names)}
+    step_ms = float(np.mean(tm.durations("s0", "s6")))
+    return wall * 1e3, step_ms, stages
+
+
+def cpu_baseline(q, k, v, w, budget_s=15.0, max_tiles=48):
+    """The float64 oracle, untuned, on one head of the same workload: Hilbert
+    order, permute, routing for that head, then block-sparse attention on as
+    many of its q-blocks as fit the time budget."""
+    from oracle import attention as oat
+    from oracle import hilbert as ohb
+    from oracle import route as ort
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    h = 0
+    qh0 = q[h:h + 1].float().cpu().numpy()
+    kh0 = k[h:h + 1].float().cpu().numpy()
+    vh0 = v[h:h + 1].float().cpu().numpy()
+    t0 = time.perf_counter()
+    perm, _ = ohb.hilbert_order(*w.grid)
+    qh, kh, vh = (ort.permute_rows(x.astype(np.float64), perm) for x in (qh0, kh0, vh0))
+    r = ort.route(qh, kh, w.block, w.p, w.k)
+    nb = r["kv_count"].shape[1]
+    rng = np.random.default_rng(1234)
+    order = rng.permutation(nb)
+    flops = 0.0
+    done = 0
+    n = qh.shape[1]
+    sizes = np.full(nb, w.block, dtype=np.int64)
+    sizes[-1] = n - (nb - 1) * w.block
+    for i in order[:max_tiles]:
+        kept = r["kv_index"][0, i, :r["kv_count"][0, i]]
+        oat.block_sparse_attention_tile(qh, kh, vh, 0, int(i), w.block, kept)
+        flops += 4.0 * sizes[i] * sizes[kept].sum() * w.d
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"head 0 of {w.heads}: oracle Hilbert order + permute + routing "
+                      f"({nb} q-blocks) + float64 block-sparse attention on {done} "
+                      f"random q-blocks; {dt:.1f} s on the host",
+            "host_cpus": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workers", type=int, default=0, help="persistent workgroups (0 = CUs)")
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-controls", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the multi-GPU head-migration path is "
+              "design-only in this library; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    log(f"generating {w.name}: {w.note}")
+    q, k, v, meta = synth.make_inputs(w, "cuda")
+    dt = q.dtype
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=dt,
+                      n_workers=args.workers or None, device="cuda")
+    out = torch.empty_like(q)
+
+    log("timed steps")
+    wall_ms, step_ms, stages = run_steps(path, q, k, v, out, w.p, w.k, args.steps,
+                                         args.warmup)
+    flops = kept_flops(path)
+    dens = path.head_density.cpu().numpy()
+    imb = cu_imbalance(path.timing.cpu().numpy())
+    attn_ms = stages["attention"]
+    value = flops / (wall_ms * 1e-3) / 1e12
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    wl = path.worker_load.cpu().numpy()
+
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "heads": w.heads, "grid": list(w.grid), "d": w.d,
+                   "block": w.block, "p": w.p, "k": w.k, "n_workers": path.n_workers,
+                   "tokens": w.n},
+    }
+    res["attention"] = {"ms": round(attn_ms, 4), "tflops_kept": round(attn_tflops, 2),
+                        "kept_tflop": round(flops / 1e12, 4),
+                        "density_mean": round(float(dens.mean()), 5),
+                        "density_min": round(float(dens.min()), 5),
+                        "density_max": round(float(dens.max()), 5)}
+    res["stages_ms"] = {k2: round(v2, 4) for k2, v2 in stages.items()}
+    route_bytes = (2 * w.heads * w.n * w.d * 2 + w.heads * path.nb ** 2
+                   + 4 * int(path.head_load.sum().item()) + 4 * w.heads * path.nb)
+    res["route"] = {"ms": round(stages["route"], 4), "algorithmic_bytes": route_bytes,
+                    "gbs": round(route_bytes / (stages["route"] * 1e-3) / 1e9, 1)}
+    res["imbalance"] = dict(imb, predicted_lpt_max_over_mean=float(wl.max() / wl.mean()))
+    traffic = read_traffic(w.name)
+    res["roofline"] = {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                       "traffic": traffic, "kernel": "attn_mfma_kernel<128,128,persistent>"}
+
+    if not args.no_controls:
+        log("head-major control")
+        o2 = torch.empty_like(q)
+        _, _, st_grid = run_steps(path, q, k, v, o2, w.p, w.k, max(2, args.dense_steps), 1,
+                                  balanced=False)
+        log("dense p=1 control")
+        _, _, st_dense = run_steps(path, q, k, v, o2, 1.0, 0, args.dense_steps, 1)
+        dense_flops = kept_flops(path)
+        res["controls"] = {
+            "head_major_attention_ms": round(st_grid["attention"], 4),
+            "lpt_speedup_over_head_major": round(st_grid["attention"] / attn_ms, 4),
+            "dense_attention_ms": round(st_dense["attention"], 4),
+            "dense_tflops": round(dense_flops / (st_dense["attention"] * 1e-3) / 1e12, 2),
+            "speedup_vs_dense_attention": round(st_dense["attention"] / attn_ms, 4),
+            "path_speedup_vs_dense_attention": round(
+                st_dense["attention"] / (stages["route"] + stages["schedule"] + attn_ms), 4),
+        }
+    res["context"] = {"pages_attention_speedup_vs_flashattention_8xH20": 4.41,
+                      "pages_dit_speedup_8xH20": "2.02-2.11",
+                      "pages_imbalance_before_after_rlb_8xH20": "1.34 -> 1.08",
+                      "pages_attention_share_of_generation_1xH20": 0.741}
+    if not args.no_cpu_baseline:
+        log("cpu oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(q, k, v, w)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

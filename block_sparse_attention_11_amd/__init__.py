@@ -6,6 +6,6 @@ a missing library raises ImportError (there is no fallback path).
 """
 from ._lib import (BF16, EINVAL, ELAUNCH, EUNSUPPORTED, EWORKSPACE, F32, OK,  # noqa: F401
                    FvattnError, declared_symbols, hilbert_permute, library_path,
-                   load_library, permute_rows, route, route_workspace_size,
+                   load_library, pack_v, permute_rows, route, route_workspace_size,
                    schedule, schedule_workspace_size, sparse_attn, status_string)
 from .pipeline import FVAttnPath, default_workers  # noqa: F401

@@ -21,6 +21,8 @@ HEADER = os.path.join(ROOT, "include", "fvattn.h")
 
 OK, EINVAL, EUNSUPPORTED, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
+SCHED_TILE_ORDER = 1
+V_ROWS, V_TILES = 0, 1
 
 _c_void_p = ctypes.c_void_p
 _c_int = ctypes.c_int
@@ -34,17 +36,19 @@ _SIGNATURES = {
                                         _c_void_p]),
     "fvattn_permute_rows": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                      _c_int, _c_int, _c_void_p]),
+    "fvattn_pack_v": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
+                               _c_int, _c_int, _c_void_p]),
     "fvattn_route_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "fvattn_route": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                               _c_int, _c_float, _c_int, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                               _c_void_p]),
     "fvattn_schedule_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int]),
-    "fvattn_schedule": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p,
+    "fvattn_schedule": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _c_size_t, _c_void_p]),
     "fvattn_sparse_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                                    _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_float, _c_void_p, _c_void_p, _c_void_p,
                                     _c_void_p, _c_int, _c_void_p, _c_void_p]),
 }
@@ -139,6 +143,19 @@ def permute_rows(src: torch.Tensor, dst: torch.Tensor, index: torch.Tensor):
         _ptr(src), _ptr(dst), _ptr(index), H, n, d, _dtype_code(src), _stream(src)))
 
 
+def pack_v(src: torch.Tensor, dst: torch.Tensor, index: torch.Tensor, block: int):
+    """dst [heads, nB, d, block] <- rows of src [heads, n, d] gathered by index,
+    one transposed tile per key block (padding keys zero)."""
+    _dev(src, dst, index)
+    _need(src.dim() == 3 and src.dtype == dst.dtype, "src [heads, n, d]")
+    H, n, d = src.shape
+    nb = (n + block - 1) // block
+    _need(dst.numel() == H * nb * d * block, "dst must hold heads*nB*d*block")
+    _need(index.dtype == torch.int32 and index.numel() == n, "index int32[n]")
+    _check("fvattn_pack_v", load_library().fvattn_pack_v(
+        _ptr(src), _ptr(dst), _ptr(index), H, n, d, block, _dtype_code(src), _stream(src)))
+
+
 def route_workspace_size(heads: int, n: int, d: int, block: int) -> int:
     return int(load_library().fvattn_route_workspace_size(heads, n, d, block))
 
@@ -167,7 +184,7 @@ def schedule_workspace_size(heads: int, n_qblocks: int, n_workers: int) -> int:
 
 
 def schedule(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
-             worker_load, workspace):
+             worker_load, workspace, tile_order: bool = False):
     _dev(kv_count, lpt_order, worker_offsets, worker_tiles, worker_load, workspace)
     _need(kv_count.dim() == 2 and kv_count.dtype == torch.int32, "kv_count i32[H, nB]")
     H, nb = kv_count.shape
@@ -178,18 +195,25 @@ def schedule(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
           "worker_load i64[W]")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("fvattn_schedule", load_library().fvattn_schedule(
-        _ptr(kv_count), H, nb, int(n_workers), _ptr(lpt_order), _ptr(worker_offsets),
+        _ptr(kv_count), H, nb, int(n_workers), SCHED_TILE_ORDER if tile_order else 0,
+        _ptr(lpt_order), _ptr(worker_offsets),
         _ptr(worker_tiles), _ptr(worker_load), _ptr(workspace), ws_bytes,
         _stream(kv_count)))
 
 
 def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
-                worker_tiles=None, n_workers: int = 0, timing=None, scale: float = 0.0):
+                worker_tiles=None, n_workers: int = 0, timing=None, scale: float = 0.0,
+                v_tiles: bool = False):
+    """v is [H, n, d] (v_tiles=False) or [H, nB, d, block] tiles (v_tiles=True)."""
     _dev(q, k, v, o, kv_count, kv_index)
-    _need(q.shape == k.shape == v.shape == o.shape and q.dim() == 3, "q,k,v,o [H, n, d]")
+    _need(q.shape == k.shape == o.shape and q.dim() == 3, "q,k,o [H, n, d]")
     _need(q.dtype == k.dtype == v.dtype == o.dtype, "one dtype")
     H, n, d = q.shape
     nb = (n + block - 1) // block
+    if v_tiles:
+        _need(v.numel() == H * nb * d * block, "v tiles [H, nB, d, block]")
+    else:
+        _need(v.shape == q.shape, "v [H, n, d]")
     _need(kv_count.numel() == H * nb and kv_index.numel() == H * nb * nb, "kv lists")
     if worker_offsets is not None:
         _dev(worker_offsets, worker_tiles)
@@ -200,5 +224,5 @@ def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
               "timing u64[W][4]")
     _check("fvattn_sparse_attn", load_library().fvattn_sparse_attn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), H, n, d, block,
-        float(scale), _ptr(kv_count), _ptr(kv_index), _ptr(worker_offsets),
+        V_TILES if v_tiles else V_ROWS, float(scale), _ptr(kv_count), _ptr(kv_index), _ptr(worker_offsets),
         _ptr(worker_tiles), int(n_workers), _ptr(timing), _stream(q)))

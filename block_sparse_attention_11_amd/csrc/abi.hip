@@ -56,6 +56,18 @@ int fvattn_permute_rows(const void* src, void* dst, const int32_t* index, int he
       src, dst, index, heads, n, (size_t)d * elem_size(dtype), stream));
 }
 
+int fvattn_pack_v(const void* src, void* dst, const int32_t* index, int heads, int n,
+                  int d, int block, int dtype, hipStream_t stream) {
+  if (!src || !dst || !index) return FVATTN_EINVAL;
+  if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
+  if (src == dst) return FVATTN_EINVAL;
+  if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
+  if (!fits_int32(nblocks(n, block) * block * (long long)d)) return FVATTN_EINVAL;
+  if (dtype != FVATTN_BF16 || block % 4 != 0 || d % 8 != 0) return FVATTN_EUNSUPPORTED;
+  if (nblocks(n, block) > 65535) return FVATTN_EUNSUPPORTED;
+  return launch_status(fvattn::launch_pack_v(src, dst, index, heads, n, d, block, stream));
+}
+
 size_t fvattn_route_workspace_size(int heads, int n, int d, int block) {
   if (heads < 1 || n < 1 || d < 1 || block < 1) return 0;
   return fvattn::route_workspace_bytes(heads, n, d, block);
@@ -87,29 +99,31 @@ size_t fvattn_schedule_workspace_size(int heads, int n_qblocks, int n_workers) {
 }
 
 int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks, int n_workers,
-                    int32_t* lpt_order, int32_t* worker_offsets, int32_t* worker_tiles,
-                    int64_t* worker_load, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
+                    int flags, int32_t* lpt_order, int32_t* worker_offsets,
+                    int32_t* worker_tiles, int64_t* worker_load, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
   if (!kv_count || !lpt_order || !worker_offsets || !worker_tiles || !worker_load)
     return FVATTN_EINVAL;
   if (heads < 1 || n_qblocks < 1 || n_workers < 1) return FVATTN_EINVAL;
   if (!fits_int32((long long)heads * n_qblocks)) return FVATTN_EINVAL;
+  if (flags & ~FVATTN_SCHED_TILE_ORDER) return FVATTN_EINVAL;
   if (n_workers > fvattn::kMaxWorkers) return FVATTN_EUNSUPPORTED;
   const size_t need = fvattn::schedule_workspace_bytes(heads, n_qblocks, n_workers);
   if (!workspace || workspace_bytes < need) return FVATTN_EWORKSPACE;
-  return launch_status(fvattn::launch_schedule(kv_count, heads * n_qblocks, n_workers,
-                                               lpt_order, worker_offsets, worker_tiles,
-                                               worker_load, workspace, stream));
+  return launch_status(fvattn::launch_schedule(
+      kv_count, heads * n_qblocks, n_workers, (flags & FVATTN_SCHED_TILE_ORDER) != 0,
+      lpt_order, worker_offsets, worker_tiles, worker_load, workspace, stream));
 }
 
 int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int dtype,
-                       int heads, int n, int d, int block, float scale,
+                       int heads, int n, int d, int block, int v_layout, float scale,
                        const int32_t* kv_count, const int32_t* kv_index,
                        const int32_t* worker_offsets, const int32_t* worker_tiles,
                        int n_workers, uint64_t* timing, hipStream_t stream) {
   if (!q || !k || !v || !o || !kv_count || !kv_index) return FVATTN_EINVAL;
   if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
   if (isnan(scale) || isinf(scale)) return FVATTN_EINVAL;
+  if (v_layout != FVATTN_V_ROWS && v_layout != FVATTN_V_TILES) return FVATTN_EINVAL;
   if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
   const int64_t nb = nblocks(n, block);
   if (!fits_int32((long long)heads * nb) || !fits_int32(nb * nb)) return FVATTN_EINVAL;
@@ -118,6 +132,10 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   }
   const bool bf16 = dtype == FVATTN_BF16;
   if (!fvattn::attn_has_mfma_instance(bf16, d, block) && (d > 128 || block > 256))
+    return FVATTN_EUNSUPPORTED;
+  // the tiled-V kernel addresses each tensor with one 32-bit buffer offset
+  if (v_layout == FVATTN_V_TILES &&
+      (long long)heads * nb * block * d * 2 > 0x7fffffffLL)
     return FVATTN_EUNSUPPORTED;
   if (timing && !worker_offsets) return FVATTN_EINVAL;
   fvattn::AttnArgs a;
@@ -138,6 +156,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   a.worker_tiles = worker_tiles;
   a.n_workers = worker_offsets ? n_workers : 0;
   a.timing = timing;
+  a.v_tiles = v_layout == FVATTN_V_TILES;
   return launch_status(fvattn::launch_sparse_attn(a, bf16, stream));
 }
 

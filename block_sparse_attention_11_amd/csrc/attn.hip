@@ -67,8 +67,13 @@ __device__ inline uint32_t bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -95,6 +100,7 @@ __device__ inline void store_elem<bf16s>(bf16s* p, float v) {
 // Plain fp32 kernel.
 // ---------------------------------------------------------------------------
 constexpr int kSimpleThreads = 256;
+constexpr float kRescaleSlack = 8.0f;
 constexpr int kSimpleChunk = 32;
 
 template <typename T, int DMAX, bool PERSIST>
@@ -141,7 +147,10 @@ __global__ __launch_bounds__(kSimpleThreads) void attn_simple_kernel(AttnArgs a)
           const int row = kc + kr;
           const bool ok = row < r1 && c < d;
           Ks[kr][c] = ok ? load_elem(K + (hb + row) * d + c) : 0.f;
-          Vs[kr][c] = ok ? load_elem(V + (hb + row) * d + c) : 0.f;
+          const size_t vi = a.v_tiles
+              ? (((size_t)h * nb + j) * d + c) * blk + (row - r0)
+              : (hb + row) * d + c;
+          Vs[kr][c] = ok ? load_elem(V + vi) : 0.f;
         }
         __syncthreads();
         if (active) {
@@ -327,17 +336,25 @@ __global__ __launch_bounds__(2 * BLK) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      // m_new stays -inf only if every score so far is masked
-      const bool none = m_new == -INFINITY;
-      const float alpha = none ? 1.f : exp2f(m_run - m_new);
-      const float m_sub = none ? 0.f : m_new;
-      m_run = m_new;
-      l_run *= alpha;
+      // Lazy rescale: the reference max m_run only moves when this block's
+      // max exceeds it by more than kRescaleSlack (log2 units), so the
+      // exponentials stay below 2^kRescaleSlack and O / l are rescaled about
+      // once per tile instead of once per block.  Any m_run gives the same
+      // softmax; only rounding differs.
+      const float mxs = mx * sl2;
+      const bool grow = mxs > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mxs : m_run;
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc_o[dt][e] *= alpha;
+          for (int e = 0; e < 16; ++e) acc_o[dt][e] *= alpha;
+      }
+      // every score of this row may be masked only if m_run is still -inf
+      const float m_sub = m_run == -INFINITY ? 0.f : m_run;
 
       // P = exp2(S * sl2 - m), rounded to bf16 in accumulator order
       uint32_t pk[BLK / 32][8];
@@ -345,8 +362,8 @@ __global__ __launch_bounds__(2 * BLK) void attn_mfma_kernel(AttnArgs a) {
       for (int kt = 0; kt < BLK / 32; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
-          const float p0 = exp2f(fmaf(s[kt][e], sl2, -m_sub));
-          const float p1 = exp2f(fmaf(s[kt][e + 1], sl2, -m_sub));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][e], sl2, -m_sub));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][e + 1], sl2, -m_sub));
           l_run += p0 + p1;
           pk[kt][e >> 1] = pack_bf16x2(p0, p1);
         }
@@ -392,6 +409,315 @@ __global__ __launch_bounds__(2 * BLK) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel fed by LDS DMA, for V stored as transposed key-block tiles
+// ([heads][nb][d][block], see launch_pack_v).  K rows and V^T tiles go from
+// HBM/L2 straight into LDS with buffer_load ... lds (no staging registers);
+// out-of-range K rows of the short last block read as zero through the
+// buffer descriptor's size.  Per key block three barriers order the work:
+//   A: K_j has landed and every wave is done with V_{j-1}  -> start V_j DMA
+//      S_j = K_j Q^T
+//   B: every wave is done with K_j                         -> start K_{j+1} DMA
+//      softmax of S_j
+//   C: V_j has landed
+//      O += V_j^T P_j^T
+// so V_j streams in during S_j and the softmax, and K_{j+1} during the
+// softmax and the PV product; two workgroups per CU cover the rest.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate for gfx9: wait until at most N vector-memory loads are
+// outstanding (exp and lgkm counters left at their maxima).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for LDS hand-offs only: this wave's LDS reads are complete,
+// then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
+// vector-memory loads, so LDS-DMA copies keep streaming across it; callers
+// wait for the copies they need with wait_vmcnt.  The memory clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D, int BLK>
+__device__ inline uint32_t vt_off(int dd, int chunk, int half) {
+  constexpr int CPR = BLK / 8;    // 16-byte chunks of a V^T row
+  return (uint32_t)(dd * (2 * BLK) + ((chunk ^ (dd & (CPR - 1))) << 4) + half * 8);
+}
+
+// read-only table entry through the scalar cache (the tables are not written
+// while the kernel runs and the index is wave-uniform)
+__device__ inline int32_t ld_uniform(const int32_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(p));
+}
+
+template <int D, int BLK, bool PERSIST>
+__global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer descriptors exist only in the device pass
+  using S = MfmaShape<D, BLK>;
+  constexpr int NW = S::kWaves;
+  constexpr int CPRK = D / 8;                 // 16-byte chunks per K row
+  constexpr int CPRV = BLK / 8;               // 16-byte chunks per V^T row
+  constexpr int KDMA = BLK * CPRK / (64 * NW);   // DMA instructions per wave, K
+  constexpr int VDMA = D * CPRV / (64 * NW);     // and V
+  static_assert(KDMA * 64 * NW == BLK * CPRK && VDMA * 64 * NW == D * CPRV, "DMA split");
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks[BLK * D * 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs[D * BLK * 2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;
+  const int g = lane >> 5;
+  const int n = a.n, nb = a.nb;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  uint16_t* O = static_cast<uint16_t*>(a.o);
+  const float sl2 = a.scale_log2;
+  // one descriptor per tensor (the host checks both fit 32-bit offsets); K
+  // rows past the end of the tensor read as zero, rows past the end of a head
+  // read the next head's rows, which the score mask removes
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.k, (short)0, (int)((size_t)a.heads * n * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.v, (short)0, (int)((size_t)a.heads * nb * D * BLK * 2), 0x00020000);
+
+  // per-lane DMA source offsets inside one block (bytes), fixed for the kernel
+  uint32_t koff[KDMA], voff[VDMA];
+#pragma unroll
+  for (int x = 0; x < KDMA; ++x) {
+    const int P = (x * NW + wave) * 64 + lane;           // LDS chunk this lane fills
+    const int r = P / CPRK, pc = P % CPRK;
+    koff[x] = (uint32_t)(r * D * 2 + (pc ^ (r & (CPRK - 1))) * 16);
+  }
+#pragma unroll
+  for (int x = 0; x < VDMA; ++x) {
+    const int P = (x * NW + wave) * 64 + lane;
+    const int dd = P / CPRV, pc = P % CPRV;
+    voff[x] = (uint32_t)(dd * BLK * 2 + (pc ^ (dd & (CPRV - 1))) * 16);
+  }
+  auto dma_k = [&](int h, int j) {
+    const uint32_t base = (uint32_t)(((size_t)h * n + (size_t)j * BLK) * D * 2);
+#pragma unroll
+    for (int x = 0; x < KDMA; ++x)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krs, (lds_void*)(Ks + (x * NW + wave) * 1024), 16, koff[x], base, 0, 0);
+  };
+  auto dma_v = [&](int h, int j) {
+    const uint32_t base = (uint32_t)(((size_t)h * nb + j) * D * BLK * 2);
+#pragma unroll
+    for (int x = 0; x < VDMA; ++x)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (lds_void*)(Vs + (x * NW + wave) * 1024), 16, voff[x], base, 0, 0);
+  };
+
+  uint64_t t0 = 0;
+  if (PERSIST && a.timing && tid == 0) stamp_start(t0);
+
+  int beg = blockIdx.x, end = blockIdx.x + 1;
+  if (PERSIST) {
+    beg = ld_uniform(a.worker_offsets + blockIdx.x);
+    end = ld_uniform(a.worker_offsets + blockIdx.x + 1);
+  }
+  // tile id, its kept count and list; entries outside [0, nB) are clamped
+  auto tile_at = [&](int it) {
+    return PERSIST ? ld_uniform(a.worker_tiles + it) : it;
+  };
+  auto count_of = [&](int tile) { return min(ld_uniform(a.kv_count + tile), nb); };
+  auto block_of = [&](int tile, int jj) {
+    return min(max(ld_uniform(a.kv_index + (size_t)tile * nb + jj), 0), nb - 1);
+  };
+  auto zero_rows = [&](int tile) {   // a tile with no kept block
+    const int hh = tile / nb, ii = tile - hh * nb;
+    const int qr = ii * BLK + wave * 32 + col;
+    if (qr < n) {
+      uint16_t* orow = O + ((size_t)hh * n + qr) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * r4 + 4 * g) = u32x2{0u, 0u};
+    }
+  };
+  // first non-empty tile at or after it (zero-filling the empty ones)
+  auto advance = [&](int it, int& tile, int& cnt) {
+    while (it < end) {
+      tile = tile_at(it);
+      cnt = count_of(tile);
+      if (cnt > 0) break;
+      zero_rows(tile);
+      ++it;
+    }
+    return it;
+  };
+
+  int tile = 0, cnt = 0;
+  int it = advance(beg, tile, cnt);
+  bf16x8 qf[D / 16];
+  f32x16 acc_o[D / 32];
+  float m_run = -INFINITY, l_run = 0.f;
+  auto start_tile = [&](int tl) {
+    const int hh = tl / nb, ii = tl - hh * nb;
+    const int qr = ii * BLK + wave * 32 + col;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (qr < n) w = *reinterpret_cast<const u32x4*>(Q + ((size_t)hh * n + qr) * D + 16 * kk + 8 * g);
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc_o[dt][e] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+  int jj = 0;
+  int j = 0;
+  if (it < end) {
+    start_tile(tile);
+    j = block_of(tile, 0);
+    dma_k(tile / nb, j);
+  }
+  while (it < end) {
+    const int h = tile / nb;
+    const int i = tile - h * nb;
+    // the (tile, block) pair after this one
+    int tile2 = tile, cnt2 = cnt, jj2 = jj + 1, it2 = it;
+    if (jj2 >= cnt) {
+      it2 = advance(it + 1, tile2, cnt2);
+      jj2 = 0;
+    }
+    const bool more = it2 < end;
+    const int jn = more ? block_of(tile2, jj2) : j;      // last: harmless reload
+
+    wait_vmcnt<0>();
+    lds_barrier();                                     // A
+    dma_v(h, j);
+
+    f32x16 s[BLK / 32];
+#pragma unroll
+    for (int kt = 0; kt < BLK / 32; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(Ks + k_off<D>(32 * kt + col, 2 * kk + g));
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
+                                                        qf[kk], s[kt], 0, 0, 0);
+      }
+    }
+    lds_barrier();                                     // B
+    dma_k(more ? tile2 / nb : h, jn);
+
+    const int r0 = j * BLK;
+    if (r0 + BLK > n) {
+#pragma unroll
+      for (int kt = 0; kt < BLK / 32; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = r0 + 32 * kt + 8 * (e >> 2) + 4 * g + (e & 3);
+          if (key >= n) s[kt][e] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < BLK / 32; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mxs = mx * sl2;
+    const bool grow = mxs > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mxs : m_run;
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc_o[dt][e] *= alpha;
+    }
+    const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+    uint32_t pk[BLK / 32][8];
+#pragma unroll
+    for (int kt = 0; kt < BLK / 32; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][e], sl2, -m_sub));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][e + 1], sl2, -m_sub));
+        l_run += p0 + p1;
+        pk[kt][e >> 1] = pack_bf16x2(p0, p1);
+      }
+
+    wait_vmcnt<KDMA>();                                // V_j landed (K_next may fly)
+    lds_barrier();                                     // C
+#pragma unroll
+    for (int c = 0; c < BLK / 16; ++c) {
+      const u32x4 pb = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1],
+                        pk[c >> 1][4 * (c & 1) + 2], pk[c >> 1][4 * (c & 1) + 3]};
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int dd = 32 * dt + col;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(Vs + vt_off<D, BLK>(dd, 2 * c, g));
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(Vs + vt_off<D, BLK>(dd, 2 * c + 1, g));
+        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                            bop, acc_o[dt], 0, 0, 0);
+      }
+    }
+
+    if (jj2 == 0) {
+      // tile finished: normalise and store, then set up the next one
+      const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const int qrow = i * BLK + wave * 32 + col;
+      if (qrow < n) {
+        uint16_t* orow = O + ((size_t)h * n + qrow) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int d0 = 32 * dt + 8 * r4 + 4 * g;
+            const u32x2 w = {pack_bf16x2(acc_o[dt][4 * r4 + 0] * inv, acc_o[dt][4 * r4 + 1] * inv),
+                             pack_bf16x2(acc_o[dt][4 * r4 + 2] * inv, acc_o[dt][4 * r4 + 3] * inv)};
+            *reinterpret_cast<u32x2*>(orow + d0) = w;
+          }
+      }
+      if (more) start_tile(tile2);
+    }
+    tile = tile2;
+    cnt = cnt2;
+    jj = jj2;
+    it = it2;
+    j = jn;
+  }
+  wait_vmcnt<0>();        // no LDS copy may outlive the workgroup
+  if (PERSIST && a.timing) {
+    __syncthreads();
+    if (tid == 0) stamp_end(a.timing, blockIdx.x, t0);
+  }
+#endif
+}
+
+template <int D, int BLK>
+hipError_t launch_mfma_dma(const AttnArgs& a, hipStream_t s) {
+  using S = MfmaShape<D, BLK>;
+  if (a.worker_offsets) {
+    hipLaunchKernelGGL((attn_mfma_dma_kernel<D, BLK, true>), dim3(a.n_workers),
+                       dim3(S::kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_mfma_dma_kernel<D, BLK, false>), dim3(a.heads * a.nb),
+                       dim3(S::kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <int D, int BLK>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t s) {
   using S = MfmaShape<D, BLK>;
@@ -432,6 +758,12 @@ bool attn_has_mfma_instance(bool bf16, int d, int block) {
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, bool bf16, hipStream_t s) {
+  if (attn_has_mfma_instance(bf16, a.d, a.block) && a.v_tiles) {
+    if (a.d == 128 && a.block == 128) return launch_mfma_dma<128, 128>(a, s);
+    if (a.d == 64 && a.block == 64) return launch_mfma_dma<64, 64>(a, s);
+    if (a.d == 64 && a.block == 128) return launch_mfma_dma<64, 128>(a, s);
+    return launch_mfma_dma<128, 64>(a, s);
+  }
   if (attn_has_mfma_instance(bf16, a.d, a.block)) {
     if (a.d == 128 && a.block == 128) return launch_mfma<128, 128>(a, s);
     if (a.d == 64 && a.block == 64) return launch_mfma<64, 64>(a, s);

@@ -22,6 +22,9 @@ hipError_t launch_hilbert(int T, int Y, int X, int32_t* perm, int32_t* inv,
 hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* index,
                                int heads, int n, size_t row_bytes,
                                hipStream_t s);
+// bf16 only; requires block % 4 == 0 and d % 8 == 0
+hipError_t launch_pack_v(const void* src, void* dst, const int32_t* index, int heads,
+                         int n, int d, int block, hipStream_t s);
 
 // ---- route.hip -------------------------------------------------------------
 struct RouteWorkspace {
@@ -42,9 +45,9 @@ constexpr int kMaxWorkers = 1024;
 constexpr int kMaxCost = 16383;
 size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers);
 hipError_t launch_schedule(const int32_t* kv_count, int tiles, int n_workers,
-                           int32_t* lpt_order, int32_t* worker_offsets,
-                           int32_t* worker_tiles, int64_t* worker_load,
-                           void* ws, hipStream_t s);
+                           bool tile_order, int32_t* lpt_order, int32_t* worker_offsets,
+                           int32_t* worker_tiles, int64_t* worker_load, void* ws,
+                           hipStream_t s);
 
 // ---- attn.hip --------------------------------------------------------------
 struct AttnArgs {
@@ -60,6 +63,7 @@ struct AttnArgs {
   const int32_t* worker_tiles;
   int n_workers;
   uint64_t* timing;               // null or [n_workers][4]
+  bool v_tiles;                   // V as [heads][nb][d][block] transposed tiles
 };
 bool attn_has_mfma_instance(bool bf16, int d, int block);
 hipError_t launch_sparse_attn(const AttnArgs& a, bool bf16, hipStream_t s);

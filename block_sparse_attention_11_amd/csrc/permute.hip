@@ -51,7 +51,57 @@ hipError_t launch_typed(const void* src, void* dst, const int32_t* index,
   return hipGetLastError();
 }
 
+// dst[h][j][c][key] = src[h][index[j*block + key]][c] for key < rows of block j,
+// 0 for the padding keys of the last block: V in Hilbert order, stored as one
+// transposed [d][block] tile per key block.  A thread moves a 4-key x 8-column
+// unit: four 16-byte row loads, eight 8-byte stores (byte shuffles with
+// v_perm_b32); lanes are laid out key-group fastest so that each group of 32
+// lanes writes 256 contiguous bytes of one tile row.
+__global__ __launch_bounds__(kPermuteThreads) void pack_v_kernel(
+    const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+    const int32_t* __restrict__ index, int n, int d, int block, int nb) {
+  const int h = blockIdx.z;
+  const int j = blockIdx.y;
+  const int kgroups = block / 4;
+  const int units = kgroups * (d / 8);
+  const int g = blockIdx.x * kPermuteThreads + threadIdx.x;
+  if (g >= units) return;
+  const int kq = g % kgroups;
+  const int c8 = g / kgroups;
+  const uint16_t* sh = src + (size_t)h * n * d;
+  uint4 rows[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int r = j * block + 4 * kq + x;
+    rows[x] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < n) rows[x] = *reinterpret_cast<const uint4*>(sh + (size_t)index[r] * d + 8 * c8);
+  }
+  uint16_t* tile = dst + (((size_t)h * nb + j) * d) * block;
+#pragma unroll
+  for (int dd = 0; dd < 8; ++dd) {
+    const uint32_t w0 = dd < 2 ? rows[0].x : dd < 4 ? rows[0].y : dd < 6 ? rows[0].z : rows[0].w;
+    const uint32_t w1 = dd < 2 ? rows[1].x : dd < 4 ? rows[1].y : dd < 6 ? rows[1].z : rows[1].w;
+    const uint32_t w2 = dd < 2 ? rows[2].x : dd < 4 ? rows[2].y : dd < 6 ? rows[2].z : rows[2].w;
+    const uint32_t w3 = dd < 2 ? rows[3].x : dd < 4 ? rows[3].y : dd < 6 ? rows[3].z : rows[3].w;
+    const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+    uint2 o;
+    o.x = __builtin_amdgcn_perm(w1, w0, sel);
+    o.y = __builtin_amdgcn_perm(w3, w2, sel);
+    *reinterpret_cast<uint2*>(tile + (size_t)(8 * c8 + dd) * block + 4 * kq) = o;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pack_v(const void* src, void* dst, const int32_t* index, int heads,
+                         int n, int d, int block, hipStream_t s) {
+  const int nb = (n + block - 1) / block;
+  const int units = (block / 4) * (d / 8);
+  hipLaunchKernelGGL(pack_v_kernel, dim3((units + kPermuteThreads - 1) / kPermuteThreads, nb, heads),
+                     dim3(kPermuteThreads), 0, s, (const uint16_t*)src, (uint16_t*)dst,
+                     index, n, d, block, nb);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* index,
                                int heads, int n, size_t row_bytes,

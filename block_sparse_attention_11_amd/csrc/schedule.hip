@@ -22,9 +22,17 @@
 //                      and one update.  Loads are kept relative to a running
 //                      base so they fit 32 bits.
 //   lpt_scatter_kernel writes each tile at worker_offsets[w] + its position in
-//                      w's list.
+//                      w's list (assignment order), or
+//   lpt_sort_kernel    run again with key = owner, which groups the tiles by
+//                      worker with ascending tile ids inside each list (tile
+//                      order: the same assignment and loads, executed
+//                      head-major inside every worker so that concurrently
+//                      running workgroups share K/V blocks in L2).
 #include "device_util.h"
 #include "internal.h"
+
+// wavefront reduction from the ROCm device library (DPP based)
+extern "C" __device__ uint32_t __ockl_wfred_min_u32(uint32_t);
 
 namespace fvattn {
 namespace {
@@ -40,6 +48,7 @@ struct SchedWs {
   int32_t* id_b;
   int32_t* owner;   // worker of the k-th tile in LPT order
   int32_t* slot;    // its position in that worker's list
+  int32_t* owner_by_tile;  // worker of tile t
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -51,14 +60,17 @@ SchedWs carve(void* ws, int tiles) {
                  reinterpret_cast<int32_t*>(b + 2 * one),
                  reinterpret_cast<int32_t*>(b + 3 * one),
                  reinterpret_cast<int32_t*>(b + 4 * one),
-                 reinterpret_cast<int32_t*>(b + 5 * one)};
+                 reinterpret_cast<int32_t*>(b + 5 * one),
+                 reinterpret_cast<int32_t*>(b + 6 * one)};
 }
 
 __device__ inline int clamp_cost(int c) { return min(max(c, 0), kMaxCost); }
 
+// by_owner == false: ids sorted by (cost desc, id asc) -> out (lpt_order)
+// by_owner == true:  ids sorted by (owner asc, id asc)  -> out (worker_tiles)
 __global__ __launch_bounds__(kSortThreads) void lpt_sort_kernel(
     const int32_t* __restrict__ cost, int tiles, SchedWs ws,
-    int32_t* __restrict__ lpt_order) {
+    int32_t* __restrict__ lpt_order, bool by_owner) {
   __shared__ int32_t table[kRadix * kSortThreads];   // [digit][thread], 64 KB
   __shared__ int32_t s_scan[kSortThreads / kWave];
   __shared__ int32_t s_max[kSortThreads / kWave];
@@ -66,8 +78,9 @@ __global__ __launch_bounds__(kSortThreads) void lpt_sort_kernel(
   const int per = (tiles + kSortThreads - 1) / kSortThreads;
   const int lo = min(tiles, tid * per), hi = min(tiles, lo + per);
 
+  const int32_t* src = by_owner ? ws.owner_by_tile : cost;
   int mx = 0;
-  for (int t = lo; t < hi; ++t) mx = max(mx, clamp_cost(cost[t]));
+  for (int t = lo; t < hi; ++t) mx = max(mx, clamp_cost(src[t]));
   mx = block_reduce<kSortThreads>(mx, s_max, [](int a, int b) { return max(a, b); });
   int bits = 0;
   while ((1 << bits) <= mx) ++bits;
@@ -79,11 +92,12 @@ __global__ __launch_bounds__(kSortThreads) void lpt_sort_kernel(
   int32_t* kout = ws.key_b;
   int32_t* iout = ws.id_b;
   for (int t = lo; t < hi; ++t) {
-    kin[t] = mx - clamp_cost(cost[t]);
+    const int c = clamp_cost(src[t]);
+    kin[t] = by_owner ? c : mx - c;
     iin[t] = t;
   }
   if (passes == 0) {
-    // every cost is zero: identity order
+    // every key is zero: identity order
     for (int t = lo; t < hi; ++t) lpt_order[t] = t;
     return;
   }
@@ -150,15 +164,19 @@ __global__ __launch_bounds__(kWave) void lpt_assign_kernel(
 
   for (int k0 = 0; k0 < tiles; k0 += kWave) {
     const int kk = k0 + lane;
-    int my_cost = 0;
-    if (kk < tiles) my_cost = clamp_cost(cost[lpt_order[kk]]);
+    int my_tile = 0, my_cost = 0;
+    if (kk < tiles) {
+      my_tile = lpt_order[kk];
+      my_cost = clamp_cost(cost[my_tile]);
+    }
     int my_owner = 0, my_slot = 0;
     const int nstep = min(kWave, tiles - k0);
     for (int j = 0; j < nstep; ++j) {
-      const uint32_t c = (uint32_t)__shfl(my_cost, j, kWave);
-      const uint32_t gmin = wave_min(lmin);
+      // broadcast the j-th tile's cost, find the least-loaded worker
+      const uint32_t c = (uint32_t)__builtin_amdgcn_readlane(my_cost, j);
+      const uint32_t gmin = __ockl_wfred_min_u32(lmin);
       const uint64_t hit = __ballot(lmin == gmin);
-      const int L = __ffsll((unsigned long long)hit) - 1;
+      const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
       int w = 0, pos = 0;
       if (lane == L) {
         bool done = false;
@@ -176,8 +194,8 @@ __global__ __launch_bounds__(kWave) void lpt_assign_kernel(
 #pragma unroll
         for (int s = 0; s < PER; ++s) lmin = min(lmin, rel[s]);
       }
-      w = __shfl(w, L, kWave);
-      pos = __shfl(pos, L, kWave);
+      w = __builtin_amdgcn_readlane(w, L);
+      pos = __builtin_amdgcn_readlane(pos, L);
       if (lane == j) {
         my_owner = w;
         my_slot = pos;
@@ -196,6 +214,7 @@ __global__ __launch_bounds__(kWave) void lpt_assign_kernel(
     if (kk < tiles) {
       ws.owner[kk] = my_owner;
       ws.slot[kk] = my_slot;
+      ws.owner_by_tile[my_tile] = my_owner;
     }
   }
   // loads and list offsets
@@ -228,16 +247,16 @@ __global__ __launch_bounds__(256) void lpt_scatter_kernel(
 size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers) {
   (void)n_workers;
   const size_t tiles = (size_t)heads * n_qblocks;
-  return 6 * align_up(sizeof(int32_t) * tiles, 256);
+  return 7 * align_up(sizeof(int32_t) * tiles, 256);
 }
 
 hipError_t launch_schedule(const int32_t* kv_count, int tiles, int n_workers,
-                           int32_t* lpt_order, int32_t* worker_offsets,
-                           int32_t* worker_tiles, int64_t* worker_load,
-                           void* wsp, hipStream_t s) {
+                           bool tile_order, int32_t* lpt_order, int32_t* worker_offsets,
+                           int32_t* worker_tiles, int64_t* worker_load, void* wsp,
+                           hipStream_t s) {
   SchedWs ws = carve(wsp, tiles);
   hipLaunchKernelGGL(lpt_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, kv_count,
-                     tiles, ws, lpt_order);
+                     tiles, ws, lpt_order, false);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int per = (n_workers + kWave - 1) / kWave;
@@ -252,8 +271,13 @@ hipError_t launch_schedule(const int32_t* kv_count, int tiles, int n_workers,
 #undef FV_ASSIGN
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lpt_scatter_kernel, dim3((tiles + 255) / 256), dim3(256), 0, s,
-                     lpt_order, tiles, ws, worker_offsets, worker_tiles);
+  if (tile_order) {
+    hipLaunchKernelGGL(lpt_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, kv_count,
+                       tiles, ws, worker_tiles, true);
+  } else {
+    hipLaunchKernelGGL(lpt_scatter_kernel, dim3((tiles + 255) / 256), dim3(256), 0, s,
+                       lpt_order, tiles, ws, worker_offsets, worker_tiles);
+  }
   return hipGetLastError();
 }
 

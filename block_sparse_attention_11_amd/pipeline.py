@@ -4,7 +4,8 @@ Allocation and call order only; each step is one C-ABI call into the HIP
 library:
 
     hilbert_permute  (once per grid shape)
-    permute_rows     Q, K, V -> Hilbert order
+    permute_rows     Q, K -> Hilbert order
+    pack_v           V -> Hilbert order, one transposed tile per key block
     route            pooled-Q/K Top-p + Top-k -> mask, kept lists, head load
     schedule         LPT work list over (head, q-block) tiles
     sparse_attn      persistent block-sparse attention over the kept blocks
@@ -26,21 +27,27 @@ def default_workers(device=None) -> int:
 
 class FVAttnPath:
     def __init__(self, heads: int, grid, d: int, block: int, dtype=torch.bfloat16,
-                 n_workers: int | None = None, device="cuda"):
+                 n_workers: int | None = None, device="cuda", tile_order: bool = True,
+                 v_tiles: bool | None = None):
         self.heads, self.grid, self.d, self.block = heads, tuple(grid), d, block
         T, Y, X = self.grid
         self.n = T * Y * X
         self.nb = (self.n + block - 1) // block
         self.dtype = dtype
+        self.tile_order = tile_order
         self.device = torch.device(device)
         self.n_workers = n_workers or default_workers(self.device)
         H, n, nb, dev = heads, self.n, self.nb, self.device
         i32 = dict(dtype=torch.int32, device=dev)
         self.perm = torch.empty(n, **i32)
         self.inv_perm = torch.empty(n, **i32)
+        # V goes to transposed key-block tiles when the bf16 tile packer applies
+        can_tile = dtype == torch.bfloat16 and d % 8 == 0 and block % 4 == 0
+        self.v_tiles = can_tile if v_tiles is None else (v_tiles and can_tile)
         self.qh = torch.empty((H, n, d), dtype=dtype, device=dev)
         self.kh = torch.empty_like(self.qh)
-        self.vh = torch.empty_like(self.qh)
+        self.vh = (torch.empty((H, nb, d, block), dtype=dtype, device=dev) if self.v_tiles
+                   else torch.empty_like(self.qh))
         self.oh = torch.empty_like(self.qh)
         self.mask = torch.empty((H, nb, nb), dtype=torch.uint8, device=dev)
         self.kv_count = torch.empty((H, nb), **i32)
@@ -67,7 +74,10 @@ class FVAttnPath:
     def to_hilbert(self, q, k, v):
         _lib.permute_rows(q, self.qh, self.perm)
         _lib.permute_rows(k, self.kh, self.perm)
-        _lib.permute_rows(v, self.vh, self.perm)
+        if self.v_tiles:
+            _lib.pack_v(v, self.vh, self.perm, self.block)
+        else:
+            _lib.permute_rows(v, self.vh, self.perm)
 
     def route(self, p: float, k_floor: int):
         _lib.route(self.qh, self.kh, self.block, p, k_floor, self.mask, self.kv_count,
@@ -75,17 +85,18 @@ class FVAttnPath:
 
     def schedule(self):
         _lib.schedule(self.kv_count, self.n_workers, self.lpt_order, self.worker_offsets,
-                      self.worker_tiles, self.worker_load, self.sched_ws)
+                      self.worker_tiles, self.worker_load, self.sched_ws,
+                      tile_order=self.tile_order)
 
     def attend(self, balanced: bool = True, timing: bool = True):
         if balanced:
             _lib.sparse_attn(self.qh, self.kh, self.vh, self.oh, self.block,
                              self.kv_count, self.kv_index, self.worker_offsets,
                              self.worker_tiles, self.n_workers,
-                             self.timing if timing else None)
+                             self.timing if timing else None, v_tiles=self.v_tiles)
         else:
             _lib.sparse_attn(self.qh, self.kh, self.vh, self.oh, self.block,
-                             self.kv_count, self.kv_index)
+                             self.kv_count, self.kv_index, v_tiles=self.v_tiles)
 
     def to_tokens(self, out):
         _lib.permute_rows(self.oh, out, self.inv_perm)

@@ -53,6 +53,14 @@ extern "C" {
 #define FVATTN_F32 0
 #define FVATTN_BF16 1
 
+/* fvattn_schedule flags. */
+#define FVATTN_SCHED_TILE_ORDER 1
+
+/* V layouts accepted by fvattn_sparse_attn. */
+#define FVATTN_V_ROWS 0    /* [heads][n][d], like Q and K                     */
+#define FVATTN_V_TILES 1   /* [heads][nB][d][block]: one transposed tile per
+                              key block, padding keys zero (fvattn_pack_v)   */
+
 /* Static string naming a status code. */
 const char* fvattn_status_string(int status);
 
@@ -87,6 +95,19 @@ int fvattn_hilbert_permute(int T, int Y, int X, int32_t* perm,
 int fvattn_permute_rows(const void* src, void* dst, const int32_t* index,
                         int heads, int n, int d, int dtype,
                         hipStream_t stream);
+
+/*
+ * Row gather into transposed key-block tiles, used for V:
+ *   dst[h][j][c][r] = src[h][index[j*block + r]][c]   for j*block + r < n,
+ *   dst[h][j][c][r] = 0                               for the padding rows
+ *                                                     of the last block.
+ * dst holds heads * nB * d * block elements (FVATTN_V_TILES layout).  The
+ * attention kernels read V^T as the A operand of the P.V product; producing
+ * it inside the Hilbert gather costs no extra memory traffic.
+ * bf16 only; block % 4 == 0, d % 8 == 0 (else FVATTN_EUNSUPPORTED).
+ */
+int fvattn_pack_v(const void* src, void* dst, const int32_t* index, int heads,
+                  int n, int d, int block, int dtype, hipStream_t stream);
 
 /*
  * Routing: block importance from mean-pooled Q/K, Top-p cut, Top-k floor.
@@ -141,16 +162,22 @@ int fvattn_route(const void* q, const void* k, int dtype, int heads, int n,
  *   worker_offsets int32 [n_workers+1], exclusive prefix of list sizes;
  *   worker_tiles   int32 [heads*n_qblocks], the lists concatenated;
  *   worker_load    int64 [n_workers], summed cost per worker.
- * Bit-exact: there is exactly one correct result per input.
+ * flags:
+ *   0                        each list in assignment order;
+ *   FVATTN_SCHED_TILE_ORDER  each list sorted by ascending tile id.  Same
+ *                            assignment and loads; a persistent kernel then
+ *                            walks heads in step across workgroups, so K/V
+ *                            blocks are shared in L2 while they run.
+ * Bit-exact: there is exactly one correct result per input and flag.
  * Limits: 1 <= n_workers <= 1024; costs in [0, 65535]; heads*n_qblocks < 2^31.
  * workspace: at least fvattn_schedule_workspace_size() bytes.
  */
 size_t fvattn_schedule_workspace_size(int heads, int n_qblocks, int n_workers);
 int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
-                    int n_workers, int32_t* lpt_order, int32_t* worker_offsets,
-                    int32_t* worker_tiles, int64_t* worker_load,
-                    void* workspace, size_t workspace_bytes,
-                    hipStream_t stream);
+                    int n_workers, int flags, int32_t* lpt_order,
+                    int32_t* worker_offsets, int32_t* worker_tiles,
+                    int64_t* worker_load, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Block-sparse attention over the kept blocks.
@@ -164,6 +191,11 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
  * written as zeros.
  *
  * scale <= 0 selects 1/sqrt(d).
+ * v_layout: FVATTN_V_ROWS or FVATTN_V_TILES (see fvattn_pack_v); Q, K and O
+ * are always [heads][n][d].  With FVATTN_V_TILES the V tiles must fit in 2 GiB
+ * (else FVATTN_EUNSUPPORTED).
+ * kv_index entries must lie in [0, nB): the MFMA kernels clamp others into
+ * that range, the plain kernel skips them (memory-safe, result undefined).
  * Work distribution:
  *   worker_offsets != NULL: persistent launch of n_workers workgroups;
  *     workgroup w runs the tiles worker_tiles[worker_offsets[w] ..
@@ -174,12 +206,13 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
  *   {start, end} of each workgroup on the 100 MHz constant clock
  *   (s_memrealtime), the raw HW_ID register and the XCC_ID register.
  * Kernels: bf16 with (d, block) in {(64, 64), (128, 128), (64, 128),
- * (128, 64)} runs on the MFMA kernel; every other (dtype, d <= 128,
- * block <= 256) combination runs on a plain fp32 VALU kernel.
+ * (128, 64)} runs on an MFMA kernel (the LDS-DMA one for FVATTN_V_TILES);
+ * every other (dtype, d <= 128, block <= 256) combination runs on a plain
+ * fp32 VALU kernel.
  */
 int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o,
                        int dtype, int heads, int n, int d, int block,
-                       float scale, const int32_t* kv_count,
+                       int v_layout, float scale, const int32_t* kv_count,
                        const int32_t* kv_index, const int32_t* worker_offsets,
                        const int32_t* worker_tiles, int n_workers,
                        uint64_t* timing, hipStream_t stream);

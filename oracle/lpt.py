@@ -36,8 +36,11 @@ def lpt_order(costs: np.ndarray) -> np.ndarray:
     return np.lexsort((t, -costs)).astype(np.int32)
 
 
-def lpt_schedule(costs: np.ndarray, n_workers: int):
-    """Greedy LPT.  Returns (order, worker_offsets, worker_tiles, worker_load)."""
+def lpt_schedule(costs: np.ndarray, n_workers: int, tile_order: bool = False):
+    """Greedy LPT.  Returns (order, worker_offsets, worker_tiles, worker_load).
+
+    tile_order=True lists each worker's tiles by ascending tile id instead of
+    in assignment order (same assignment, same loads)."""
     if n_workers < 1:
         raise ValueError("n_workers must be >= 1")
     costs = np.asarray(costs, dtype=np.int64).reshape(-1)
@@ -48,6 +51,8 @@ def lpt_schedule(costs: np.ndarray, n_workers: int):
         w = int(np.argmin(loads))          # argmin returns the lowest index on ties
         lists[w].append(int(t))
         loads[w] += costs[t]
+    if tile_order:
+        lists = [sorted(x) for x in lists]
     sizes = np.array([len(x) for x in lists], dtype=np.int64)
     offsets = np.zeros(n_workers + 1, dtype=np.int32)
     offsets[1:] = np.cumsum(sizes)

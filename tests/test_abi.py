@@ -24,7 +24,7 @@ def test_library_is_built_in_tree():
 def test_exports_every_declared_symbol():
     lib = _lib.load_library()
     declared = _lib.declared_symbols()
-    assert len(declared) == 9, declared
+    assert len(declared) == 10, declared
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
@@ -51,7 +51,7 @@ def test_workspace_sizes():
     rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert lib.fvattn_route_workspace_size(40, 75600, 128, 128) == 2 * rnd(pooled) + rnd(scores)
     assert lib.fvattn_route_workspace_size(0, 75600, 128, 128) == 0
-    assert lib.fvattn_schedule_workspace_size(40, 591, 256) == 6 * rnd(40 * 591 * 4)
+    assert lib.fvattn_schedule_workspace_size(40, 591, 256) == 7 * rnd(40 * 591 * 4)
     assert lib.fvattn_schedule_workspace_size(40, 591, 0) == 0
 
 
@@ -82,18 +82,26 @@ def _validation_main():
         (lib.fvattn_route(P, P, 1, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, N, 1 << 30, N), EWS),
         (lib.fvattn_route(P, P, 1, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, P, 16, N), EWS),
         # schedule
-        (lib.fvattn_schedule(P, 40, 591, 1025, P, P, P, P, P, 1 << 30, N), EUNS),
-        (lib.fvattn_schedule(P, 40, 591, 0, P, P, P, P, P, 1 << 30, N), EINVAL),
-        (lib.fvattn_schedule(N, 40, 591, 256, P, P, P, P, P, 1 << 30, N), EINVAL),
-        (lib.fvattn_schedule(P, 40, 591, 256, P, P, P, P, P, 100, N), EWS),
+        (lib.fvattn_schedule(P, 40, 591, 1025, 0, P, P, P, P, P, 1 << 30, N), EUNS),
+        (lib.fvattn_schedule(P, 40, 591, 256, 2, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule(P, 40, 591, 0, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule(N, 40, 591, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule(P, 40, 591, 256, 1, P, P, P, P, P, 100, N), EWS),
         # attention
-        (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0.0, P, P, N, N, 0, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0.0, P, P, N, N, 0, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 256, 16, 0.0, P, P, N, N, 0, N, N), EUNS),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, float("inf"), P, P, N, N, 0, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0.0, P, P, P, N, 4, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0.0, P, P, P, P, 0, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0.0, P, P, N, N, 0, P, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 0.0, P, P, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 0.0, P, P, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 256, 16, 0, 0.0, P, P, N, N, 0, N, N), EUNS),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, float("inf"), P, P, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 0.0, P, P, P, N, 4, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 0.0, P, P, P, P, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 0.0, P, P, N, N, 0, P, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 2, 0.0, P, P, N, N, 0, N, N), EINVAL),
+        # pack_v
+        (lib.fvattn_pack_v(P, P, P, 1, 128, 64, 16, 1, N), EINVAL),
+        (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 16, 0, N), EUNS),
+        (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 60, 16, 1, N), EUNS),
+        (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 18, 1, N), EUNS),
+        (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), N, 1, 128, 64, 16, 1, N), EINVAL),
     ]
     bad = [(i, got, want) for i, (got, want) in enumerate(checks) if got != want]
     if bad:

@@ -74,6 +74,25 @@ def test_permute_rows_bit_exact(dtype, d):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("d,block,n", [(128, 128, 75600 // 40), (64, 64, 390), (64, 16, 105),
+                                       (128, 64, 1000), (8, 4, 9)])
+def test_pack_v_bit_exact(d, block, n):
+    say(f"pack_v d={d} block={block} n={n}")
+    g = torch.Generator().manual_seed(11)
+    H = 3
+    x = torch.randn((H, n, d), generator=g).to(torch.bfloat16)
+    idx = torch.randperm(n, generator=g).to(torch.int32)
+    nb = (n + block - 1) // block
+    dst = torch.full((H, nb, d, block), 7.0, dtype=torch.bfloat16, device=DEV)
+    _lib.pack_v(x.to(DEV), dst, idx.to(DEV), block)
+    torch.cuda.synchronize()
+    xs = ort.permute_rows(x.view(torch.int16).numpy(), idx.numpy())      # [H, n, d]
+    pad = np.zeros((H, nb * block, d), dtype=np.int16)
+    pad[:, :n] = xs
+    ref = pad.reshape(H, nb, block, d).transpose(0, 1, 3, 2)
+    assert np.array_equal(dst.cpu().view(torch.int16).numpy(), ref)
+
+
 # ---------------------------------------------------------------------------
 # Routing
 # ---------------------------------------------------------------------------
@@ -157,7 +176,7 @@ def test_route_parity(name, p, kf):
 # ---------------------------------------------------------------------------
 # LPT schedule
 # ---------------------------------------------------------------------------
-def gpu_schedule(costs_2d, W):
+def gpu_schedule(costs_2d, W, tile_order=False):
     H, nb = costs_2d.shape
     kvc = torch.from_numpy(costs_2d.astype(np.int32)).to(DEV)
     tiles = H * nb
@@ -166,7 +185,7 @@ def gpu_schedule(costs_2d, W):
     wt = torch.empty(tiles, dtype=torch.int32, device=DEV)
     wl = torch.empty(W, dtype=torch.int64, device=DEV)
     ws = torch.empty(_lib.schedule_workspace_size(H, nb, W), dtype=torch.uint8, device=DEV)
-    _lib.schedule(kvc, W, order, off, wt, wl, ws)
+    _lib.schedule(kvc, W, order, off, wt, wl, ws, tile_order=tile_order)
     torch.cuda.synchronize()
     return order.cpu().numpy(), off.cpu().numpy(), wt.cpu().numpy(), wl.cpu().numpy()
 
@@ -184,9 +203,10 @@ SCHED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("tile_order", [False, True])
 @pytest.mark.parametrize("name,costs,W", SCHED_CASES)
-def test_schedule_bit_exact(name, costs, W):
-    say(f"schedule {name} W={W}")
+def test_schedule_bit_exact(name, costs, W, tile_order):
+    say(f"schedule {name} W={W} tile_order={tile_order}")
     rng = np.random.default_rng(sum(map(ord, name)))
     if name == "random_ties":
         costs = rng.integers(1, 9, size=(8, 37))
@@ -196,8 +216,8 @@ def test_schedule_bit_exact(name, costs, W):
         costs = rng.integers(8, 1155, size=(40, 1154))
     elif name == "big_costs":
         costs = rng.integers(0, 16384, size=(5, 333))
-    got = gpu_schedule(costs, W)
-    ref = olpt.lpt_schedule(costs.reshape(-1), W)
+    got = gpu_schedule(costs, W, tile_order)
+    ref = olpt.lpt_schedule(costs.reshape(-1), W, tile_order=tile_order)
     for g, r, what in zip(got, ref, ("order", "offsets", "tiles", "loads")):
         assert np.array_equal(g, r), what
 
@@ -210,12 +230,13 @@ ATTN_CASES = ["tiny", "small", "ragged_f32", "ragged_bf16", "mid_bf16", "mid_bf1
 
 @pytest.mark.parametrize("name", ATTN_CASES)
 @pytest.mark.parametrize("balanced", [True, False])
-def test_attention_parity(name, balanced):
+@pytest.mark.parametrize("v_tiles", [True, False])
+def test_attention_parity(name, balanced, v_tiles):
     w = workload(name)
-    say(f"attention {name} balanced={balanced}")
+    say(f"attention {name} balanced={balanced} v_tiles={v_tiles}")
     q, k, v, _ = synth.make_inputs(w, "cpu")
     path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, n_workers=7,
-                      device=DEV)
+                      device=DEV, v_tiles=v_tiles)
     out = path.run(q.to(DEV), k.to(DEV), v.to(DEV), w.p, w.k, balanced=balanced)
     torch.cuda.synchronize()
     perm = path.perm.cpu().numpy()
@@ -250,13 +271,27 @@ def test_dense_control_matches_brute_force(name):
     assert err["max_abs"] <= tol["max_abs"] and err["rel_l2"] <= tol["rel_l2"], err
 
 
-@pytest.mark.parametrize("dtype,d,block", [(torch.bfloat16, 128, 128),
-                                           (torch.bfloat16, 64, 64),
-                                           (torch.float32, 64, 16)])
-def test_attention_handmade_lists(dtype, d, block):
+def attn_call(q, k, v, o, block, cnt, idx, v_tiles, **kw):
+    """sparse_attn with V given as rows or packed into tiles (identity order)."""
+    if v_tiles:
+        H, n, d = v.shape
+        nb = (n + block - 1) // block
+        vt = torch.empty((H, nb, d, block), dtype=v.dtype, device=DEV)
+        _lib.pack_v(v, vt, torch.arange(n, dtype=torch.int32, device=DEV), block)
+        v = vt
+    _lib.sparse_attn(q, k, v, o, block, cnt, idx, v_tiles=v_tiles, **kw)
+
+
+@pytest.mark.parametrize("dtype,d,block,v_tiles", [(torch.bfloat16, 128, 128, True),
+                                                   (torch.bfloat16, 128, 128, False),
+                                                   (torch.bfloat16, 64, 64, True),
+                                                   (torch.bfloat16, 64, 64, False),
+                                                   (torch.bfloat16, 64, 16, True),
+                                                   (torch.float32, 64, 16, False)])
+def test_attention_handmade_lists(dtype, d, block, v_tiles):
     """Edge cases: an empty row (written as zeros), a single kept block, only
     the short tail block, and constant V rows."""
-    say(f"handmade lists {dtype} d={d} block={block}")
+    say(f"handmade lists {dtype} d={d} block={block} v_tiles={v_tiles}")
     H, n = 2, 3 * block + block // 2 + 1
     nb = 4
     g = torch.Generator().manual_seed(3)
@@ -273,8 +308,8 @@ def test_attention_handmade_lists(dtype, d, block):
     idx[1, 2, :3] = [0, 2, 3]
     idx[1, 3, 0] = 3
     o = torch.full((H, n, d), float("nan"), dtype=dtype, device=DEV)
-    _lib.sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), o, block,
-                     torch.from_numpy(cnt).to(DEV), torch.from_numpy(idx).to(DEV))
+    attn_call(q.to(DEV), k.to(DEV), v.to(DEV), o, block,
+              torch.from_numpy(cnt).to(DEV), torch.from_numpy(idx).to(DEV), v_tiles)
     torch.cuda.synchronize()
     got = to_np(o)
     qq, kk, vv = (to_np(x).astype(np.float64) for x in (q, k, v))
@@ -287,8 +322,8 @@ def test_attention_handmade_lists(dtype, d, block):
     assert err["max_abs"] <= tol["max_abs"] and err["rel_l2"] <= tol["rel_l2"], err
     # constant V rows give the constant, whatever the mask
     vc = torch.arange(d, dtype=torch.float32).div(d).expand(H, n, d).contiguous().to(dtype)
-    _lib.sparse_attn(q.to(DEV), k.to(DEV), vc.to(DEV), o, block,
-                     torch.from_numpy(cnt).to(DEV), torch.from_numpy(idx).to(DEV))
+    attn_call(q.to(DEV), k.to(DEV), vc.to(DEV), o, block,
+              torch.from_numpy(cnt).to(DEV), torch.from_numpy(idx).to(DEV), v_tiles)
     torch.cuda.synchronize()
     got = to_np(o)
     exp = to_np(vc)

@@ -84,3 +84,16 @@ def test_equal_costs_spread_evenly():
     _, off, _, loads = lpt.lpt_schedule(costs, 5)
     assert loads.max() - loads.min() <= 7
     assert np.diff(off).tolist() == [5, 5, 5, 4, 4]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tile_order_keeps_the_assignment(seed):
+    rng = np.random.default_rng(200 + seed)
+    costs = rng.integers(0, 30, size=int(rng.integers(1, 200)))
+    W = int(rng.integers(1, 17))
+    o1, off1, t1, l1 = lpt.lpt_schedule(costs, W)
+    o2, off2, t2, l2 = lpt.lpt_schedule(costs, W, tile_order=True)
+    assert (o1 == o2).all() and (off1 == off2).all() and (l1 == l2).all()
+    for w in range(W):
+        a, b = t1[off1[w]:off1[w + 1]], t2[off2[w]:off2[w + 1]]
+        assert sorted(a.tolist()) == b.tolist()
