@@ -205,6 +205,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-controls", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the multi-GPU head-migration path is "
@@ -219,6 +221,16 @@ def main():
     path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=dt,
                       n_workers=args.workers or None, device="cuda")
     out = torch.empty_like(q)
+
+    if args.copy_calibration:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
+        # the scale between the counters and bytes moved
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     log("timed steps")
     wall_ms, step_ms, stages = run_steps(path, q, k, v, out, w.p, w.k, args.steps,

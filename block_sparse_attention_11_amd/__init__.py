@@ -4,7 +4,7 @@ with a thin ctypes binding.
 Importing the package loads nothing; the library is loaded on first use and
 a missing library raises ImportError (there is no fallback path).
 """
-from ._lib import (BF16, EINVAL, ELAUNCH, EUNSUPPORTED, EWORKSPACE, F32, OK,  # noqa: F401
+from ._lib import (BF16, attn_workers, EINVAL, ELAUNCH, EUNSUPPORTED, EWORKSPACE, F32, OK,  # noqa: F401
                    FvattnError, declared_symbols, hilbert_permute, library_path,
                    load_library, pack_v, permute_rows, route, route_workspace_size,
                    schedule, schedule_workspace_size, sparse_attn, status_string)

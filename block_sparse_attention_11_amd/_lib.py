@@ -47,6 +47,8 @@ _SIGNATURES = {
     "fvattn_schedule": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _c_size_t, _c_void_p]),
+    "fvattn_attn_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int,
+                                     ctypes.POINTER(_c_int)]),
     "fvattn_sparse_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_float, _c_void_p, _c_void_p, _c_void_p,
@@ -226,3 +228,12 @@ def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), H, n, d, block,
         V_TILES if v_tiles else V_ROWS, float(scale), _ptr(kv_count), _ptr(kv_index), _ptr(worker_offsets),
         _ptr(worker_tiles), int(n_workers), _ptr(timing), _stream(q)))
+
+
+def attn_workers(dtype: torch.dtype, d: int, block: int, v_tiles: bool) -> int:
+    """Resident workgroups of the attention kernel on the current device."""
+    out = _c_int(0)
+    code = F32 if dtype == torch.float32 else BF16
+    _check("fvattn_attn_workers", load_library().fvattn_attn_workers(
+        code, d, block, V_TILES if v_tiles else V_ROWS, ctypes.byref(out)))
+    return int(out.value)

@@ -160,4 +160,18 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   return launch_status(fvattn::launch_sparse_attn(a, bf16, stream));
 }
 
+int fvattn_attn_workers(int dtype, int d, int block, int v_layout, int* workers) {
+  if (!workers || !dtype_ok(dtype) || d < 1 || block < 1) return FVATTN_EINVAL;
+  if (v_layout != FVATTN_V_ROWS && v_layout != FVATTN_V_TILES) return FVATTN_EINVAL;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FVATTN_ELAUNCH;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return FVATTN_ELAUNCH;
+  if (fvattn::attn_occupancy(dtype == FVATTN_BF16, d, block, v_layout == FVATTN_V_TILES,
+                             &per_cu) != hipSuccess)
+    return FVATTN_ELAUNCH;
+  *workers = cus * (per_cu > 0 ? per_cu : 1);
+  return FVATTN_OK;
+}
+
 }  // extern "C"

@@ -752,6 +752,36 @@ hipError_t launch_simple_any(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+template <typename K>
+hipError_t occupancy_of(K kernel, int threads, int* per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, reinterpret_cast<const void*>(kernel),
+                                                      threads, 0);
+}
+
+hipError_t attn_occupancy(bool bf16, int d, int block, bool v_tiles, int* per_cu) {
+  if (attn_has_mfma_instance(bf16, d, block)) {
+    const int threads = 2 * block;
+#define FV_OCC(D, B)                                                                       \
+  if (d == D && block == B)                                                                \
+    return v_tiles ? occupancy_of(attn_mfma_dma_kernel<D, B, true>, threads, per_cu)       \
+                   : occupancy_of(attn_mfma_kernel<D, B, true>, threads, per_cu);
+    FV_OCC(128, 128)
+    FV_OCC(64, 64)
+    FV_OCC(64, 128)
+    FV_OCC(128, 64)
+#undef FV_OCC
+  }
+  const int dm = d <= 32 ? 32 : d <= 64 ? 64 : 128;
+  if (bf16) {
+    if (dm == 32) return occupancy_of(attn_simple_kernel<bf16s, 32, true>, kSimpleThreads, per_cu);
+    if (dm == 64) return occupancy_of(attn_simple_kernel<bf16s, 64, true>, kSimpleThreads, per_cu);
+    return occupancy_of(attn_simple_kernel<bf16s, 128, true>, kSimpleThreads, per_cu);
+  }
+  if (dm == 32) return occupancy_of(attn_simple_kernel<float, 32, true>, kSimpleThreads, per_cu);
+  if (dm == 64) return occupancy_of(attn_simple_kernel<float, 64, true>, kSimpleThreads, per_cu);
+  return occupancy_of(attn_simple_kernel<float, 128, true>, kSimpleThreads, per_cu);
+}
+
 bool attn_has_mfma_instance(bool bf16, int d, int block) {
   if (!bf16) return false;
   return (d == 64 || d == 128) && (block == 64 || block == 128);

@@ -41,7 +41,7 @@ hipError_t launch_route(const void* q, const void* k, bool bf16, int heads,
                         const RouteWorkspace& ws, hipStream_t s);
 
 // ---- schedule.hip ----------------------------------------------------------
-constexpr int kMaxWorkers = 1024;
+constexpr int kMaxWorkers = 2048;
 constexpr int kMaxCost = 16383;
 size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers);
 hipError_t launch_schedule(const int32_t* kv_count, int tiles, int n_workers,
@@ -66,6 +66,8 @@ struct AttnArgs {
   bool v_tiles;                   // V as [heads][nb][d][block] transposed tiles
 };
 bool attn_has_mfma_instance(bool bf16, int d, int block);
+// resident persistent workgroups per CU of the kernel that would run
+hipError_t attn_occupancy(bool bf16, int d, int block, bool v_tiles, int* per_cu);
 hipError_t launch_sparse_attn(const AttnArgs& a, bool bf16, hipStream_t s);
 
 }  // namespace fvattn

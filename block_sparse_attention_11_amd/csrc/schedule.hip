@@ -15,12 +15,12 @@
 //                      thread owns a contiguous run of tiles; digit counts are
 //                      kept per thread in LDS and scanned in (digit, thread)
 //                      order, which makes every pass stable.
-//   lpt_assign_kernel  one wavefront: worker loads live in registers (up to 16
-//                      per lane, worker w = lane * per + slot, so "lowest
-//                      index" = lowest lane, then lowest slot); per tile a
-//                      wavefront min-reduction, a ballot for the first holder
-//                      and one update.  Loads are kept relative to a running
-//                      base so they fit 32 bits.
+//   lpt_assign_kernel  one 1024-thread workgroup, exact greedy in batches:
+//                      workers sorted by (load, index) in LDS; a run of tiles
+//                      goes to the sorted workers in order for as long as each
+//                      is still the greedy minimum (prefix-minimum test), then
+//                      the keys are re-sorted.  Near-equal costs give batches
+//                      of about one tile per worker.
 //   lpt_scatter_kernel writes each tile at worker_offsets[w] + its position in
 //                      w's list (assignment order), or
 //   lpt_sort_kernel    run again with key = owner, which groups the tiles by
@@ -30,9 +30,6 @@
 //                      running workgroups share K/V blocks in L2).
 #include "device_util.h"
 #include "internal.h"
-
-// wavefront reduction from the ROCm device library (DPP based)
-extern "C" __device__ uint32_t __ockl_wfred_min_u32(uint32_t);
 
 namespace fvattn {
 namespace {
@@ -143,96 +140,137 @@ __global__ __launch_bounds__(kSortThreads) void lpt_sort_kernel(
   }
 }
 
-template <int PER>
-__global__ __launch_bounds__(kWave) void lpt_assign_kernel(
+// Batched exact LPT.  Workers are kept sorted by key = load * 2048 + w in LDS
+// (so "smallest key" = least load, lowest index on ties).  For the next tiles
+// of the LPT order, tile k+s is tentatively given to the worker at sorted
+// position s; the greedy rule would make the same choice exactly when that
+// worker's key is below every key already raised in this batch, i.e. below
+// the prefix minimum of (key + cost << 11) over positions < s.  The batch is
+// cut at the first position where this fails, the raised keys are written
+// back and the array is re-sorted (bitonic).  Zero-cost tiles do not change
+// any load: they all go to the current minimum.
+constexpr int kAssignThreads = 1024;
+constexpr int kMaxWorkersPow2 = 2048;
+constexpr int kWorkerBits = 11;
+
+__global__ __launch_bounds__(kAssignThreads) void lpt_assign_kernel(
     const int32_t* __restrict__ cost, const int32_t* __restrict__ lpt_order,
     int tiles, int n_workers, SchedWs ws, int32_t* __restrict__ worker_offsets,
     int64_t* __restrict__ worker_load) {
-  const int lane = threadIdx.x;
-  uint32_t rel[PER];      // load - base
-  int32_t cnt[PER];
-  constexpr uint32_t kInvalid = 0xffffffffu;
-#pragma unroll
-  for (int s = 0; s < PER; ++s) {
-    rel[s] = (lane * PER + s < n_workers) ? 0u : kInvalid;
-    cnt[s] = 0;
+  __shared__ uint64_t key[kMaxWorkersPow2];
+  __shared__ uint64_t tmp[kMaxWorkersPow2];
+  __shared__ int32_t cnt[kMaxWorkersPow2];
+  __shared__ int32_t s_red[kAssignThreads / kWave];
+  __shared__ int32_t s_scan[kAssignThreads / kWave];
+  const int tid = threadIdx.x;
+  int wp = 1;
+  while (wp < n_workers) wp <<= 1;
+  constexpr uint64_t kInf = ~0ull;
+  for (int x = tid; x < wp; x += kAssignThreads) {
+    key[x] = x < n_workers ? (uint64_t)x : kInf;
+    cnt[x] = 0;
   }
-  uint64_t base = 0;
-  uint32_t lmin = kInvalid;
-#pragma unroll
-  for (int s = 0; s < PER; ++s) lmin = min(lmin, rel[s]);
+  __syncthreads();
 
-  for (int k0 = 0; k0 < tiles; k0 += kWave) {
-    const int kk = k0 + lane;
-    int my_tile = 0, my_cost = 0;
-    if (kk < tiles) {
-      my_tile = lpt_order[kk];
-      my_cost = clamp_cost(cost[my_tile]);
-    }
-    int my_owner = 0, my_slot = 0;
-    const int nstep = min(kWave, tiles - k0);
-    for (int j = 0; j < nstep; ++j) {
-      // broadcast the j-th tile's cost, find the least-loaded worker
-      const uint32_t c = (uint32_t)__builtin_amdgcn_readlane(my_cost, j);
-      const uint32_t gmin = __ockl_wfred_min_u32(lmin);
-      const uint64_t hit = __ballot(lmin == gmin);
-      const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
-      int w = 0, pos = 0;
-      if (lane == L) {
-        bool done = false;
-#pragma unroll
-        for (int s = 0; s < PER; ++s) {
-          if (!done && rel[s] == gmin) {
-            done = true;
-            w = lane * PER + s;
-            pos = cnt[s];
-            rel[s] += c;
-            cnt[s] += 1;
+  auto sort_keys = [&]() {
+    for (int kk = 2; kk <= wp; kk <<= 1) {
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        for (int x = tid; x < wp; x += kAssignThreads) {
+          const int y = x ^ jj;
+          if (y > x) {
+            const uint64_t a = key[x], b = key[y];
+            const bool up = (x & kk) == 0;
+            if (up ? (a > b) : (a < b)) {
+              key[x] = b;
+              key[y] = a;
+            }
           }
         }
-        lmin = kInvalid;
-#pragma unroll
-        for (int s = 0; s < PER; ++s) lmin = min(lmin, rel[s]);
-      }
-      w = __builtin_amdgcn_readlane(w, L);
-      pos = __builtin_amdgcn_readlane(pos, L);
-      if (lane == j) {
-        my_owner = w;
-        my_slot = pos;
-      }
-      // keep relative loads small: rebase when the minimum grows large
-      if (gmin > (1u << 30)) {
-        base += gmin;
-#pragma unroll
-        for (int s = 0; s < PER; ++s)
-          if (rel[s] != kInvalid) rel[s] -= gmin;
-        lmin = kInvalid;
-#pragma unroll
-        for (int s = 0; s < PER; ++s) lmin = min(lmin, rel[s]);
+        __syncthreads();
       }
     }
-    if (kk < tiles) {
-      ws.owner[kk] = my_owner;
-      ws.slot[kk] = my_slot;
-      ws.owner_by_tile[my_tile] = my_owner;
+  };
+
+  int k = 0;
+  while (k < tiles) {
+    const int bmax = min(n_workers, tiles - k);
+    // raised keys, and zero-cost detection
+    int zero_at = bmax;
+    for (int x = tid; x < wp; x += kAssignThreads) {
+      uint64_t nk = kInf;
+      if (x < bmax) {
+        const uint32_t c = (uint32_t)clamp_cost(cost[lpt_order[k + x]]);
+        nk = key[x] + ((uint64_t)c << kWorkerBits);
+        if (c == 0) zero_at = min(zero_at, x);
+      }
+      tmp[x] = nk;
     }
+    zero_at = block_reduce<kAssignThreads>(zero_at, s_red, [](int a, int b) { return min(a, b); });
+    if (zero_at == 0) {
+      // the rest of the order costs nothing: every remaining tile goes to
+      // the least-loaded worker, keeping its list order
+      const int w0 = (int)(key[0] & ((1u << kWorkerBits) - 1));
+      const int base = cnt[w0];
+      for (int t = k + tid; t < tiles; t += kAssignThreads) {
+        ws.owner[t] = w0;
+        ws.slot[t] = base + (t - k);
+      }
+      __syncthreads();
+      if (tid == 0) cnt[w0] = base + (tiles - k);
+      __syncthreads();
+      break;
+    }
+    // exclusive prefix minimum of tmp over positions (Hillis-Steele in LDS)
+    __syncthreads();
+    for (int off = 1; off < wp; off <<= 1) {
+      uint64_t v[kMaxWorkersPow2 / kAssignThreads];
+      int e = 0;
+      for (int x = tid; x < wp; x += kAssignThreads, ++e)
+        v[e] = x >= off ? min(tmp[x], tmp[x - off]) : tmp[x];
+      __syncthreads();
+      e = 0;
+      for (int x = tid; x < wp; x += kAssignThreads, ++e) tmp[x] = v[e];
+      __syncthreads();
+    }
+    // tmp[x] is now the inclusive prefix minimum; position s is accepted when
+    // key[s] < prefix_min(s - 1)
+    int cut = min(bmax, zero_at);
+    for (int x = tid; x < cut; x += kAssignThreads)
+      if (x > 0 && key[x] >= tmp[x - 1]) cut = min(cut, x);
+    cut = block_reduce<kAssignThreads>(cut, s_red, [](int a, int b) { return min(a, b); });
+    // assign, raise keys (each worker appears once in a batch)
+    for (int x = tid; x < cut; x += kAssignThreads) {
+      const uint64_t kx = key[x];
+      const int w = (int)(kx & ((1u << kWorkerBits) - 1));
+      const uint32_t c = (uint32_t)clamp_cost(cost[lpt_order[k + x]]);
+      ws.owner[k + x] = w;
+      ws.slot[k + x] = cnt[w];
+      cnt[w] += 1;
+      key[x] = kx + ((uint64_t)c << kWorkerBits);
+    }
+    __syncthreads();
+    sort_keys();
+    k += cut;
   }
-  // loads and list offsets
-  int my_total = 0;
-#pragma unroll
-  for (int s = 0; s < PER; ++s) my_total += cnt[s];
-  const int incl = wave_inclusive_scan(my_total);
-  int off = incl - my_total;
-#pragma unroll
-  for (int s = 0; s < PER; ++s) {
-    const int w = lane * PER + s;
-    if (w < n_workers) {
-      worker_offsets[w] = off;
-      worker_load[w] = (int64_t)(base + rel[s]);
-      off += cnt[s];
-    }
+
+  // owner by tile, list offsets and loads
+  for (int t = tid; t < tiles; t += kAssignThreads) ws.owner_by_tile[lpt_order[t]] = ws.owner[t];
+  // exclusive scan of cnt over workers: contiguous chunk per thread
+  const int per = (n_workers + kAssignThreads - 1) / kAssignThreads;
+  const int lo = min(n_workers, tid * per), hi = min(n_workers, lo + per);
+  int run = 0;
+  for (int w = lo; w < hi; ++w) run += cnt[w];
+  int total;
+  int off = block_exclusive_scan<kAssignThreads>(run, s_scan, total);
+  for (int w = lo; w < hi; ++w) {
+    worker_offsets[w] = off;
+    off += cnt[w];
   }
-  if (lane == kWave - 1) worker_offsets[n_workers] = incl;
+  if (tid == 0) worker_offsets[n_workers] = total;
+  for (int x = tid; x < n_workers; x += kAssignThreads) {
+    const uint64_t kx = key[x];
+    worker_load[kx & ((1u << kWorkerBits) - 1)] = (int64_t)(kx >> kWorkerBits);
+  }
 }
 
 __global__ __launch_bounds__(256) void lpt_scatter_kernel(
@@ -259,16 +297,8 @@ hipError_t launch_schedule(const int32_t* kv_count, int tiles, int n_workers,
                      tiles, ws, lpt_order, false);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int per = (n_workers + kWave - 1) / kWave;
-#define FV_ASSIGN(P)                                                                 \
-  hipLaunchKernelGGL(lpt_assign_kernel<P>, dim3(1), dim3(kWave), 0, s, kv_count,      \
-                     lpt_order, tiles, n_workers, ws, worker_offsets, worker_load)
-  if (per <= 1) FV_ASSIGN(1);
-  else if (per <= 2) FV_ASSIGN(2);
-  else if (per <= 4) FV_ASSIGN(4);
-  else if (per <= 8) FV_ASSIGN(8);
-  else FV_ASSIGN(16);
-#undef FV_ASSIGN
+  hipLaunchKernelGGL(lpt_assign_kernel, dim3(1), dim3(kAssignThreads), 0, s, kv_count,
+                     lpt_order, tiles, n_workers, ws, worker_offsets, worker_load);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (tile_order) {

@@ -17,9 +17,11 @@ import torch
 
 from . import _lib
 
+MAX_WORKERS = 2048          # fvattn_schedule's limit
+
 
 def default_workers(device=None) -> int:
-    """One persistent workgroup per compute unit."""
+    """Compute units of the device."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
         else torch.device(device)
     return torch.cuda.get_device_properties(dev).multi_processor_count
@@ -36,7 +38,6 @@ class FVAttnPath:
         self.dtype = dtype
         self.tile_order = tile_order
         self.device = torch.device(device)
-        self.n_workers = n_workers or default_workers(self.device)
         H, n, nb, dev = heads, self.n, self.nb, self.device
         i32 = dict(dtype=torch.int32, device=dev)
         self.perm = torch.empty(n, **i32)
@@ -49,6 +50,9 @@ class FVAttnPath:
         self.vh = (torch.empty((H, nb, d, block), dtype=dtype, device=dev) if self.v_tiles
                    else torch.empty_like(self.qh))
         self.oh = torch.empty_like(self.qh)
+        with torch.cuda.device(dev):
+            self.n_workers = n_workers or min(MAX_WORKERS,
+                                              _lib.attn_workers(dtype, d, block, self.v_tiles))
         self.mask = torch.empty((H, nb, nb), dtype=torch.uint8, device=dev)
         self.kv_count = torch.empty((H, nb), **i32)
         self.kv_index = torch.empty((H, nb, nb), **i32)

@@ -169,7 +169,7 @@ int fvattn_route(const void* q, const void* k, int dtype, int heads, int n,
  *                            walks heads in step across workgroups, so K/V
  *                            blocks are shared in L2 while they run.
  * Bit-exact: there is exactly one correct result per input and flag.
- * Limits: 1 <= n_workers <= 1024; costs in [0, 65535]; heads*n_qblocks < 2^31.
+ * Limits: 1 <= n_workers <= 2048; costs in [0, 65535]; heads*n_qblocks < 2^31.
  * workspace: at least fvattn_schedule_workspace_size() bytes.
  */
 size_t fvattn_schedule_workspace_size(int heads, int n_qblocks, int n_workers);
@@ -216,6 +216,17 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o,
                        const int32_t* kv_index, const int32_t* worker_offsets,
                        const int32_t* worker_tiles, int n_workers,
                        uint64_t* timing, hipStream_t stream);
+
+/*
+ * Persistent workers for fvattn_sparse_attn on the current device: the
+ * number of workgroups of the attention kernel that (dtype, d, block,
+ * v_layout) selects which can be resident at once (compute units times
+ * workgroups per compute unit).  Pass it as n_workers to fvattn_schedule and
+ * fvattn_sparse_attn so every compute unit stays busy.  Writes *workers;
+ * returns FVATTN_EINVAL for bad arguments and FVATTN_ELAUNCH if the HIP
+ * runtime query fails (for instance with no GPU).
+ */
+int fvattn_attn_workers(int dtype, int d, int block, int v_layout, int* workers);
 
 #ifdef __cplusplus
 }

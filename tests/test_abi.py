@@ -24,7 +24,7 @@ def test_library_is_built_in_tree():
 def test_exports_every_declared_symbol():
     lib = _lib.load_library()
     declared = _lib.declared_symbols()
-    assert len(declared) == 10, declared
+    assert len(declared) == 11, declared
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
@@ -82,7 +82,7 @@ def _validation_main():
         (lib.fvattn_route(P, P, 1, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, N, 1 << 30, N), EWS),
         (lib.fvattn_route(P, P, 1, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, P, 16, N), EWS),
         # schedule
-        (lib.fvattn_schedule(P, 40, 591, 1025, 0, P, P, P, P, P, 1 << 30, N), EUNS),
+        (lib.fvattn_schedule(P, 40, 591, 2049, 0, P, P, P, P, P, 1 << 30, N), EUNS),
         (lib.fvattn_schedule(P, 40, 591, 256, 2, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule(P, 40, 591, 0, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule(N, 40, 591, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
@@ -96,6 +96,9 @@ def _validation_main():
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 0.0, P, P, P, P, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 0.0, P, P, N, N, 0, P, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 2, 0.0, P, P, N, N, 0, N, N), EINVAL),
+        # workers
+        (lib.fvattn_attn_workers(1, 128, 128, 1, N), EINVAL),
+        (lib.fvattn_attn_workers(1, 128, 128, 5, ctypes.byref(ctypes.c_int())), EINVAL),
         # pack_v
         (lib.fvattn_pack_v(P, P, P, 1, 128, 64, 16, 1, N), EINVAL),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 16, 0, N), EUNS),

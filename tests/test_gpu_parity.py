@@ -198,6 +198,7 @@ SCHED_CASES = [
     ("equal", np.full((40, 591), 561), 256),
     ("random_ties", None, 64),
     ("random_wide", None, 1024),
+    ("max_workers", None, 2048),
     ("random_odd", None, 100),
     ("big_costs", None, 256),
 ]
@@ -210,7 +211,7 @@ def test_schedule_bit_exact(name, costs, W, tile_order):
     rng = np.random.default_rng(sum(map(ord, name)))
     if name == "random_ties":
         costs = rng.integers(1, 9, size=(8, 37))
-    elif name == "random_wide":
+    elif name in ("random_wide", "max_workers"):
         costs = rng.integers(0, 600, size=(40, 591))
     elif name == "random_odd":
         costs = rng.integers(8, 1155, size=(40, 1154))
@@ -366,3 +367,12 @@ def test_timing_records_every_worker():
     assert (t[:, 1] >= t[:, 0]).all() and (t[:, 0] > 0).all()
     # every worker ran inside one kernel launch: the spans overlap
     assert t[:, 0].max() <= t[:, 1].min() + 10_000_000
+
+
+def test_attn_workers_is_a_multiple_of_the_cus():
+    say("attn_workers")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for v_tiles in (True, False):
+        w = _lib.attn_workers(torch.bfloat16, 128, 128, v_tiles)
+        assert w >= cus and w % cus == 0
+    assert _lib.attn_workers(torch.float32, 64, 16, False) % cus == 0
