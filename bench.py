@@ -150,7 +150,7 @@ def run_steps(path, q, k, v, out, p, kf, steps, warmup, balanced=True):
     return wall * 1e3, step_ms, stages
 
 
-def cpu_baseline(q, k, v, w, budget_s=15.0, max_tiles=48):
+def cpu_baseline(q, k, v, w, budget_s=15.0, max_tiles=400):
     """The float64 oracle, untuned, on one head of the same workload: Hilbert
     order, permute, routing for that head, then block-sparse attention on as
     many of its q-blocks as fit the time budget."""

@@ -44,14 +44,15 @@ _SIGNATURES = {
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                               _c_void_p]),
     "fvattn_schedule_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int]),
-    "fvattn_schedule": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
+    "fvattn_schedule": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                 _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _c_size_t, _c_void_p]),
-    "fvattn_attn_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int,
+    "fvattn_attn_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                      ctypes.POINTER(_c_int)]),
     "fvattn_sparse_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                    _c_float, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_int, _c_float, _c_void_p, _c_void_p, _c_void_p,
                                     _c_void_p, _c_int, _c_void_p, _c_void_p]),
 }
 
@@ -186,18 +187,20 @@ def schedule_workspace_size(heads: int, n_qblocks: int, n_workers: int) -> int:
 
 
 def schedule(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
-             worker_load, workspace, tile_order: bool = False):
+             worker_load, workspace, tile_order: bool = False, group: int = 1):
+    """LPT lists over tiles of `group` q-blocks (tiles = H * ceil(nB / group))."""
     _dev(kv_count, lpt_order, worker_offsets, worker_tiles, worker_load, workspace)
     _need(kv_count.dim() == 2 and kv_count.dtype == torch.int32, "kv_count i32[H, nB]")
     H, nb = kv_count.shape
-    tiles = H * nb
+    tiles = H * ((nb + group - 1) // group)
     _need(lpt_order.numel() == tiles and worker_tiles.numel() == tiles, "tile arrays")
     _need(worker_offsets.numel() == n_workers + 1, "worker_offsets[W+1]")
     _need(worker_load.numel() == n_workers and worker_load.dtype == torch.int64,
           "worker_load i64[W]")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("fvattn_schedule", load_library().fvattn_schedule(
-        _ptr(kv_count), H, nb, int(n_workers), SCHED_TILE_ORDER if tile_order else 0,
+        _ptr(kv_count), H, nb, int(group), int(n_workers),
+        SCHED_TILE_ORDER if tile_order else 0,
         _ptr(lpt_order), _ptr(worker_offsets),
         _ptr(worker_tiles), _ptr(worker_load), _ptr(workspace), ws_bytes,
         _stream(kv_count)))
@@ -205,7 +208,7 @@ def schedule(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
 
 def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
                 worker_tiles=None, n_workers: int = 0, timing=None, scale: float = 0.0,
-                v_tiles: bool = False):
+                v_tiles: bool = False, group: int = 1):
     """v is [H, n, d] (v_tiles=False) or [H, nB, d, block] tiles (v_tiles=True)."""
     _dev(q, k, v, o, kv_count, kv_index)
     _need(q.shape == k.shape == o.shape and q.dim() == 3, "q,k,o [H, n, d]")
@@ -226,14 +229,15 @@ def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
               "timing u64[W][4]")
     _check("fvattn_sparse_attn", load_library().fvattn_sparse_attn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), H, n, d, block,
-        V_TILES if v_tiles else V_ROWS, float(scale), _ptr(kv_count), _ptr(kv_index), _ptr(worker_offsets),
+        V_TILES if v_tiles else V_ROWS, int(group), float(scale), _ptr(kv_count), _ptr(kv_index), _ptr(worker_offsets),
         _ptr(worker_tiles), int(n_workers), _ptr(timing), _stream(q)))
 
 
-def attn_workers(dtype: torch.dtype, d: int, block: int, v_tiles: bool) -> int:
+def attn_workers(dtype: torch.dtype, d: int, block: int, v_tiles: bool,
+                 group: int = 1) -> int:
     """Resident workgroups of the attention kernel on the current device."""
     out = _c_int(0)
     code = F32 if dtype == torch.float32 else BF16
     _check("fvattn_attn_workers", load_library().fvattn_attn_workers(
-        code, d, block, V_TILES if v_tiles else V_ROWS, ctypes.byref(out)))
+        code, d, block, V_TILES if v_tiles else V_ROWS, int(group), ctypes.byref(out)))
     return int(out.value)

@@ -63,7 +63,7 @@ int fvattn_pack_v(const void* src, void* dst, const int32_t* index, int heads, i
   if (src == dst) return FVATTN_EINVAL;
   if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
   if (!fits_int32(nblocks(n, block) * block * (long long)d)) return FVATTN_EINVAL;
-  if (dtype != FVATTN_BF16 || block % 4 != 0 || d % 8 != 0) return FVATTN_EUNSUPPORTED;
+  if (dtype != FVATTN_BF16 || block % 8 != 0 || d % 8 != 0) return FVATTN_EUNSUPPORTED;
   if (nblocks(n, block) > 65535) return FVATTN_EUNSUPPORTED;
   return launch_status(fvattn::launch_pack_v(src, dst, index, heads, n, d, block, stream));
 }
@@ -98,25 +98,27 @@ size_t fvattn_schedule_workspace_size(int heads, int n_qblocks, int n_workers) {
   return fvattn::schedule_workspace_bytes(heads, n_qblocks, n_workers);
 }
 
-int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks, int n_workers,
-                    int flags, int32_t* lpt_order, int32_t* worker_offsets,
+int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group,
+                    int n_workers, int flags, int32_t* lpt_order, int32_t* worker_offsets,
                     int32_t* worker_tiles, int64_t* worker_load, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   if (!kv_count || !lpt_order || !worker_offsets || !worker_tiles || !worker_load)
     return FVATTN_EINVAL;
   if (heads < 1 || n_qblocks < 1 || n_workers < 1) return FVATTN_EINVAL;
+  if (group != 1 && group != 2) return FVATTN_EINVAL;
   if (!fits_int32((long long)heads * n_qblocks)) return FVATTN_EINVAL;
   if (flags & ~FVATTN_SCHED_TILE_ORDER) return FVATTN_EINVAL;
   if (n_workers > fvattn::kMaxWorkers) return FVATTN_EUNSUPPORTED;
   const size_t need = fvattn::schedule_workspace_bytes(heads, n_qblocks, n_workers);
   if (!workspace || workspace_bytes < need) return FVATTN_EWORKSPACE;
   return launch_status(fvattn::launch_schedule(
-      kv_count, heads * n_qblocks, n_workers, (flags & FVATTN_SCHED_TILE_ORDER) != 0,
+      kv_count, heads, n_qblocks, group, n_workers, (flags & FVATTN_SCHED_TILE_ORDER) != 0,
       lpt_order, worker_offsets, worker_tiles, worker_load, workspace, stream));
 }
 
 int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int dtype,
-                       int heads, int n, int d, int block, int v_layout, float scale,
+                       int heads, int n, int d, int block, int v_layout, int group,
+                       float scale,
                        const int32_t* kv_count, const int32_t* kv_index,
                        const int32_t* worker_offsets, const int32_t* worker_tiles,
                        int n_workers, uint64_t* timing, hipStream_t stream) {
@@ -124,6 +126,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
   if (isnan(scale) || isinf(scale)) return FVATTN_EINVAL;
   if (v_layout != FVATTN_V_ROWS && v_layout != FVATTN_V_TILES) return FVATTN_EINVAL;
+  if (group != 1 && group != 2) return FVATTN_EINVAL;
   if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
   const int64_t nb = nblocks(n, block);
   if (!fits_int32((long long)heads * nb) || !fits_int32(nb * nb)) return FVATTN_EINVAL;
@@ -133,9 +136,10 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   const bool bf16 = dtype == FVATTN_BF16;
   if (!fvattn::attn_has_mfma_instance(bf16, d, block) && (d > 128 || block > 256))
     return FVATTN_EUNSUPPORTED;
-  // the tiled-V kernel addresses each tensor with one 32-bit buffer offset
+  // the tiled-V kernel addresses each tensor with one 32-bit buffer offset;
+  // tiles exist only for blocks of a multiple of 8 rows (fvattn_pack_v)
   if (v_layout == FVATTN_V_TILES &&
-      (long long)heads * nb * block * d * 2 > 0x7fffffffLL)
+      ((long long)heads * nb * block * d * 2 > 0x7fffffffLL || block % 8 != 0))
     return FVATTN_EUNSUPPORTED;
   if (timing && !worker_offsets) return FVATTN_EINVAL;
   fvattn::AttnArgs a;
@@ -157,18 +161,22 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   a.n_workers = worker_offsets ? n_workers : 0;
   a.timing = timing;
   a.v_tiles = v_layout == FVATTN_V_TILES;
+  a.group = group;
+  a.tiles_per_head = (int)((nb + group - 1) / group);
   return launch_status(fvattn::launch_sparse_attn(a, bf16, stream));
 }
 
-int fvattn_attn_workers(int dtype, int d, int block, int v_layout, int* workers) {
+int fvattn_attn_workers(int dtype, int d, int block, int v_layout, int group,
+                        int* workers) {
   if (!workers || !dtype_ok(dtype) || d < 1 || block < 1) return FVATTN_EINVAL;
   if (v_layout != FVATTN_V_ROWS && v_layout != FVATTN_V_TILES) return FVATTN_EINVAL;
+  if (group != 1 && group != 2) return FVATTN_EINVAL;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FVATTN_ELAUNCH;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return FVATTN_ELAUNCH;
   if (fvattn::attn_occupancy(dtype == FVATTN_BF16, d, block, v_layout == FVATTN_V_TILES,
-                             &per_cu) != hipSuccess)
+                             group, &per_cu) != hipSuccess)
     return FVATTN_ELAUNCH;
   *workers = cus * (per_cu > 0 ? per_cu : 1);
   return FVATTN_OK;

@@ -70,6 +70,8 @@ __device__ inline uint32_t bf16_bits(float f) {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2 v = {lo, hi};
@@ -95,6 +97,11 @@ template <>
 __device__ inline void store_elem<bf16s>(bf16s* p, float v) {
   *reinterpret_cast<uint16_t*>(p) = (uint16_t)bf16_bits(v);
 }
+
+// Marks a uniform branch body as not to be speculated: without it the
+// compiler turns rarely taken branches (the tail-block key mask, the lazy
+// rescale) into unconditional selects executed on every block.
+__device__ inline void keep_branch() { asm volatile(""); }
 
 // ---------------------------------------------------------------------------
 // Plain fp32 kernel.
@@ -123,7 +130,9 @@ __global__ __launch_bounds__(kSimpleThreads) void attn_simple_kernel(AttnArgs a)
   }
   for (int it = beg; it < end; ++it) {
     const int tile = PERSIST ? a.worker_tiles[it] : it;
-    const int h = tile / nb, i = tile - (tile / nb) * nb;
+    const int h = tile / a.tiles_per_head;
+    const int gm = tile - h * a.tiles_per_head;
+    for (int i = gm * a.group; i < min(nb, (gm + 1) * a.group); ++i) {
     const int r = i * blk + tid;
     const bool active = tid < blk && r < n;
     const size_t hb = (size_t)h * n;
@@ -147,8 +156,9 @@ __global__ __launch_bounds__(kSimpleThreads) void attn_simple_kernel(AttnArgs a)
           const int row = kc + kr;
           const bool ok = row < r1 && c < d;
           Ks[kr][c] = ok ? load_elem(K + (hb + row) * d + c) : 0.f;
+          const int kr0 = row - r0;
           const size_t vi = a.v_tiles
-              ? (((size_t)h * nb + j) * d + c) * blk + (row - r0)
+              ? (((size_t)h * nb + j) * d + c) * blk + 4 * ((kr0 >> 2) ^ vt_unit_swap(c)) + (kr0 & 3)
               : (hb + row) * d + c;
           Vs[kr][c] = ok ? load_elem(V + vi) : 0.f;
         }
@@ -176,6 +186,7 @@ __global__ __launch_bounds__(kSimpleThreads) void attn_simple_kernel(AttnArgs a)
       for (int c = 0; c < DMAX; ++c)
         if (c < d) store_elem(O + (hb + r) * d + c, acc[c] * inv);
     }
+    }  // q-blocks of the tile
   }
   if (PERSIST && a.timing) {
     __syncthreads();
@@ -240,8 +251,9 @@ __global__ __launch_bounds__(2 * BLK) void attn_mfma_kernel(AttnArgs a) {
   }
   for (int it = beg; it < end; ++it) {
     const int tile = PERSIST ? a.worker_tiles[it] : it;
-    const int h = tile / nb;
-    const int i = tile - h * nb;
+    const int h = tile / a.tiles_per_head;
+    const int gm = tile - h * a.tiles_per_head;
+    for (int i = gm * a.group; i < min(nb, (gm + 1) * a.group); ++i) {
     const size_t hb = (size_t)h * n;
     const int qrow = i * BLK + wave * 32 + col;
     const bool qvalid = qrow < n;
@@ -322,6 +334,7 @@ __global__ __launch_bounds__(2 * BLK) void attn_mfma_kernel(AttnArgs a) {
       }
       // accumulator layout: s[kt][e] is key 32*kt + 8*(e/4) + 4*g + e%4
       if (r0 + BLK > n) {
+      keep_branch();
 #pragma unroll
         for (int kt = 0; kt < BLK / 32; ++kt)
 #pragma unroll
@@ -344,6 +357,7 @@ __global__ __launch_bounds__(2 * BLK) void attn_mfma_kernel(AttnArgs a) {
       const float mxs = mx * sl2;
       const bool grow = mxs > m_run + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(grow)) {
+      keep_branch();
         const float m_new = grow ? mxs : m_run;
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
@@ -402,6 +416,7 @@ __global__ __launch_bounds__(2 * BLK) void attn_mfma_kernel(AttnArgs a) {
           *reinterpret_cast<u32x2*>(orow + d0) = w;
         }
     }
+    }  // q-blocks of the tile
   }
   if (PERSIST && a.timing) {
     __syncthreads();
@@ -474,6 +489,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
   const int wave = tid >> 6;
   const int col = lane & 31;
   const int g = lane >> 5;
+  const int vhalf = g ^ vt_unit_swap(col);     // V^T rows 32dt+col share col's bits 3, 4
   const int n = a.n, nb = a.nb;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   uint16_t* O = static_cast<uint16_t*>(a.o);
@@ -599,13 +615,17 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
     lds_barrier();                                     // A
     dma_v(h, j);
 
+    // S^T = K Q^T; the key tiles kt are independent accumulators, so they are
+    // interleaved (kk outer) to keep dependent MFMAs apart
     f32x16 s[BLK / 32];
 #pragma unroll
-    for (int kt = 0; kt < BLK / 32; ++kt) {
+    for (int kt = 0; kt < BLK / 32; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+    for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+      for (int kt = 0; kt < BLK / 32; ++kt) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(Ks + k_off<D>(32 * kt + col, 2 * kk + g));
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
                                                         qf[kk], s[kt], 0, 0, 0);
@@ -616,6 +636,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
 
     const int r0 = j * BLK;
     if (r0 + BLK > n) {
+      keep_branch();
 #pragma unroll
       for (int kt = 0; kt < BLK / 32; ++kt)
 #pragma unroll
@@ -633,6 +654,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
     const float mxs = mx * sl2;
     const bool grow = mxs > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {
+      keep_branch();
       const float m_new = grow ? mxs : m_run;
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -643,6 +665,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e) acc_o[dt][e] *= alpha;
     }
     const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+    // P in bf16; the row sum adds the same rounded values the P.V product uses
+    // (v_dot2 with (1, 1): two per instruction)
     uint32_t pk[BLK / 32][8];
 #pragma unroll
     for (int kt = 0; kt < BLK / 32; ++kt)
@@ -650,8 +674,9 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
       for (int e = 0; e < 16; e += 2) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][e], sl2, -m_sub));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][e + 1], sl2, -m_sub));
-        l_run += p0 + p1;
         pk[kt][e >> 1] = pack_bf16x2(p0, p1);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kt][e >> 1]),
+                                                kOnesBf16x2, l_run, false);
       }
 
     wait_vmcnt<KDMA>();                                // V_j landed (K_next may fly)
@@ -664,8 +689,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int dd = 32 * dt + col;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(Vs + vt_off<D, BLK>(dd, 2 * c, g));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(Vs + vt_off<D, BLK>(dd, 2 * c + 1, g));
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(Vs + vt_off<D, BLK>(dd, 2 * c, vhalf));
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(Vs + vt_off<D, BLK>(dd, 2 * c + 1, vhalf));
         const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
         acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                             bop, acc_o[dt], 0, 0, 0);
@@ -705,6 +730,304 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
 #endif
 }
 
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel for tiles of two q-blocks (group = 2), V as tiles.
+//
+// The kernel is bound by streaming K and V^T (64 KB per kept block pair at
+// d = 128), so one workgroup of 2*BLK/32 wavefronts serves two consecutive
+// q-blocks of a head and loads each key block once for both: it walks the
+// union of the two ascending kept lists, and each half of the workgroup
+// computes only on the blocks its own q-block kept.  K and V^T are double
+// buffered in four LDS arrays (the loop body is instantiated for both buffer
+// assignments, so the compiler sees distinct objects and does not wait on the
+// in-flight copy): the copy of union block u+1 is issued right after the one
+// barrier of block u and overlaps all of block u's work.
+// ---------------------------------------------------------------------------
+template <int D, int BLK, bool PERSIST>
+__global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = 2 * BLK / 32;            // wavefronts, both q-blocks
+  constexpr int CPRK = D / 8;
+  constexpr int CPRV = BLK / 8;
+  constexpr int KDMA = BLK * CPRK / (64 * NW);
+  constexpr int VDMA = D * CPRV / (64 * NW);
+  static_assert(KDMA * 64 * NW == BLK * CPRK && VDMA * 64 * NW == D * CPRV, "DMA split");
+  __shared__ __attribute__((aligned(1024))) uint8_t K0[BLK * D * 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t K1[BLK * D * 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t V0[D * BLK * 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t V1[D * BLK * 2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int grp = wave / (NW / 2);            // which q-block of the pair
+  const int wq = wave % (NW / 2);             // 32-query slice inside it
+  const int col = lane & 31;
+  const int g = lane >> 5;
+  const int vhalf = g ^ vt_unit_swap(col);
+  const int n = a.n, nb = a.nb, tph = a.tiles_per_head;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  uint16_t* O = static_cast<uint16_t*>(a.o);
+  const float sl2 = a.scale_log2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.k, (short)0, (int)((size_t)a.heads * n * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.v, (short)0, (int)((size_t)a.heads * nb * D * BLK * 2), 0x00020000);
+
+  // DMA instruction x of this wave fills LDS chunks P = (x*NW + wave)*64 + lane;
+  // consecutive x advance by NW*64 chunks = a whole number of rows that is a
+  // multiple of the swizzle period, so the source offset is affine in x
+  static_assert((NW * 64 / CPRK) % CPRK == 0 && (NW * 64 / CPRV) % CPRV == 0, "swizzle period");
+  constexpr uint32_t kStepK = (NW * 64 / CPRK) * D * 2;     // bytes per DMA step, K
+  constexpr uint32_t kStepV = (NW * 64 / CPRV) * BLK * 2;   // and V^T
+  uint32_t koff, voff;
+  {
+    const int P = wave * 64 + lane;
+    const int r = P / CPRK, pc = P % CPRK;
+    koff = (uint32_t)(r * D * 2 + (pc ^ (r & (CPRK - 1))) * 16);
+    const int dd = P / CPRV, pv = P % CPRV;
+    voff = (uint32_t)(dd * BLK * 2 + (pv ^ (dd & (CPRV - 1))) * 16);
+  }
+  auto dma = [&](uint8_t* kb, uint8_t* vb, int h, int j) {
+    const uint32_t kbase = (uint32_t)(((size_t)h * n + (size_t)j * BLK) * D * 2);
+    const uint32_t vbase = (uint32_t)(((size_t)h * nb + j) * D * BLK * 2);
+#pragma unroll
+    for (int x = 0; x < KDMA; ++x)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krs, (lds_void*)(kb + (x * NW + wave) * 1024), 16, koff, kbase + x * kStepK, 0, 0);
+#pragma unroll
+    for (int x = 0; x < VDMA; ++x)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (lds_void*)(vb + (x * NW + wave) * 1024), 16, voff, vbase + x * kStepV, 0, 0);
+  };
+
+  uint64_t t0 = 0;
+  if (PERSIST && a.timing && tid == 0) stamp_start(t0);
+  int beg = blockIdx.x, end = blockIdx.x + 1;
+  if (PERSIST) {
+    beg = ld_uniform(a.worker_offsets + blockIdx.x);
+    end = ld_uniform(a.worker_offsets + blockIdx.x + 1);
+  }
+
+  // walk state (wave-uniform): position in the worker list, the pair, the
+  // two list cursors and the current union block
+  struct Walk {
+    int it, h, i0, ca, cb, pa, pb, u;
+    bool ina, inb;
+  };
+  auto list_at = [&](int h, int i, int p) {
+    return min(max(ld_uniform(a.kv_index + ((size_t)h * nb + i) * nb + p), 0), nb - 1);
+  };
+  auto set_block = [&](Walk& w) {
+    const int ja = w.pa < w.ca ? list_at(w.h, w.i0, w.pa) : nb;
+    const int jb = w.pb < w.cb ? list_at(w.h, w.i0 + 1, w.pb) : nb;
+    w.u = min(ja, jb);
+    w.ina = ja == w.u;
+    w.inb = jb == w.u;
+  };
+  auto zero_rows = [&](int h, int i) {
+    const int qr = i * BLK + wq * 32 + col;
+    if (i < nb && qr < n) {
+      uint16_t* orow = O + ((size_t)h * n + qr) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * r4 + 4 * g) = u32x2{0u, 0u};
+    }
+  };
+  // open the tile at list position it, or the next non-empty one
+  auto open_tile = [&](Walk& w, int it) {
+    while (it < end) {
+      const int tile = PERSIST ? ld_uniform(a.worker_tiles + it) : it;
+      const int h = tile / tph;
+      const int i0 = (tile - h * tph) * 2;
+      const int ca = min(ld_uniform(a.kv_count + (size_t)h * nb + i0), nb);
+      const int cb = i0 + 1 < nb ? min(ld_uniform(a.kv_count + (size_t)h * nb + i0 + 1), nb) : 0;
+      if (ca > 0 || cb > 0) {
+        w.it = it; w.h = h; w.i0 = i0; w.ca = ca; w.cb = cb; w.pa = 0; w.pb = 0;
+        set_block(w);
+        return;
+      }
+      zero_rows(h, i0 + grp);
+      ++it;
+    }
+    w.it = end;
+  };
+  auto advance = [&](Walk w) {
+    w.pa += w.ina;
+    w.pb += w.inb;
+    if (w.pa >= w.ca && w.pb >= w.cb) open_tile(w, w.it + 1);
+    else set_block(w);
+    return w;
+  };
+
+  bf16x8 qf[D / 16];
+  f32x16 acc_o[D / 32];
+  float m_run = -INFINITY, l_run = 0.f;
+  auto start_tile = [&](const Walk& w) {
+    const int i = w.i0 + grp;
+    const int qr = i * BLK + wq * 32 + col;
+    const bool ok = i < nb && qr < n;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 v4 = {0u, 0u, 0u, 0u};
+      if (ok) v4 = *reinterpret_cast<const u32x4*>(Q + ((size_t)w.h * n + qr) * D + 16 * kk + 8 * g);
+      qf[kk] = __builtin_bit_cast(bf16x8, v4);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc_o[dt][e] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+  auto finish_tile = [&](const Walk& w) {
+    const int i = w.i0 + grp;
+    const int qr = i * BLK + wq * 32 + col;
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (i < nb && qr < n) {
+      uint16_t* orow = O + ((size_t)w.h * n + qr) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = 32 * dt + 8 * r4 + 4 * g;
+          const u32x2 o2 = {pack_bf16x2(acc_o[dt][4 * r4 + 0] * inv, acc_o[dt][4 * r4 + 1] * inv),
+                            pack_bf16x2(acc_o[dt][4 * r4 + 2] * inv, acc_o[dt][4 * r4 + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = o2;
+        }
+    }
+  };
+
+  // one union block: compute on (kc, vc), prefetch the next one into (kn, vn)
+  Walk cur;
+  open_tile(cur, beg);
+  auto step = [&](uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn) {
+    const Walk nxt = advance(cur);
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (nxt.it < end) dma(kn, vn, nxt.h, nxt.u);
+    const bool mine = grp == 0 ? cur.ina : cur.inb;
+    if (mine) {
+      // the block in halves of HK keys: an online-softmax step per half keeps
+      // the live score / probability registers small
+      constexpr int HK = BLK >= 128 ? 64 : BLK;
+      constexpr int KT = HK / 32;              // 32-key tiles per half
+      const int j = cur.u;
+      const int r0 = j * BLK;
+#pragma unroll
+      for (int half = 0; half < BLK / HK; ++half) {
+        f32x16 s[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            const int row = half * HK + 32 * kt + col;
+            const u32x4 w4 = *reinterpret_cast<const u32x4*>(kc + k_off<D>(row, 2 * kk + g));
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4),
+                                                            qf[kk], s[kt], 0, 0, 0);
+          }
+        }
+        if (r0 + half * HK + HK > n) {
+          keep_branch();
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int key = r0 + half * HK + 32 * kt + 8 * (e >> 2) + 4 * g + (e & 3);
+              if (key >= n) s[kt][e] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mxs = mx * sl2;
+        const bool grow = mxs > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          keep_branch();
+          const float m_new = grow ? mxs : m_run;
+          const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc_o[dt][e] *= alpha;
+        }
+        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+        uint32_t pk[KT][8];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][e], sl2, -m_sub));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][e + 1], sl2, -m_sub));
+            pk[kt][e >> 1] = pack_bf16x2(p0, p1);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kt][e >> 1]),
+                                                    kOnesBf16x2, l_run, false);
+          }
+        // chunk c (16 keys) of this half = accumulator registers 8*(c%2).. of tile c/2
+#pragma unroll
+        for (int c = 0; c < HK / 16; ++c) {
+          const u32x4 pb = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1],
+                            pk[c >> 1][4 * (c & 1) + 2], pk[c >> 1][4 * (c & 1) + 3]};
+          const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
+          const int cb = half * (HK / 16) + c;     // chunk index inside the block
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const int dd = 32 * dt + col;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vc + vt_off<D, BLK>(dd, 2 * cb, vhalf));
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vc + vt_off<D, BLK>(dd, 2 * cb + 1, vhalf));
+            const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+            acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                bop, acc_o[dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (nxt.it != cur.it) {
+      finish_tile(cur);
+      if (nxt.it < end) start_tile(nxt);
+    }
+    cur = nxt;
+    return cur.it < end;
+  };
+
+  if (cur.it < end) {
+    start_tile(cur);
+    dma(K0, V0, cur.h, cur.u);
+    while (step(K0, V0, K1, V1) && step(K1, V1, K0, V0)) {
+    }
+  }
+  wait_vmcnt<0>();
+  if (PERSIST && a.timing) {
+    __syncthreads();
+    if (tid == 0) stamp_end(a.timing, blockIdx.x, t0);
+  }
+#endif
+}
+
+template <int D, int BLK>
+hipError_t launch_mfma_pair(const AttnArgs& a, hipStream_t s) {
+  if (a.worker_offsets) {
+    hipLaunchKernelGGL((attn_mfma_pair_kernel<D, BLK, true>), dim3(a.n_workers),
+                       dim3(4 * BLK), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_mfma_pair_kernel<D, BLK, false>),
+                       dim3(a.heads * a.tiles_per_head), dim3(4 * BLK), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <int D, int BLK>
 hipError_t launch_mfma_dma(const AttnArgs& a, hipStream_t s) {
   using S = MfmaShape<D, BLK>;
@@ -725,7 +1048,7 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((attn_mfma_kernel<D, BLK, true>), dim3(a.n_workers),
                        dim3(S::kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((attn_mfma_kernel<D, BLK, false>), dim3(a.heads * a.nb),
+    hipLaunchKernelGGL((attn_mfma_kernel<D, BLK, false>), dim3(a.heads * a.tiles_per_head),
                        dim3(S::kThreads), 0, s, a);
   }
   return hipGetLastError();
@@ -737,7 +1060,7 @@ hipError_t launch_simple(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((attn_simple_kernel<T, DMAX, true>), dim3(a.n_workers),
                        dim3(kSimpleThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((attn_simple_kernel<T, DMAX, false>), dim3(a.heads * a.nb),
+    hipLaunchKernelGGL((attn_simple_kernel<T, DMAX, false>), dim3(a.heads * a.tiles_per_head),
                        dim3(kSimpleThreads), 0, s, a);
   }
   return hipGetLastError();
@@ -758,13 +1081,17 @@ hipError_t occupancy_of(K kernel, int threads, int* per_cu) {
                                                       threads, 0);
 }
 
-hipError_t attn_occupancy(bool bf16, int d, int block, bool v_tiles, int* per_cu) {
+hipError_t attn_occupancy(bool bf16, int d, int block, bool v_tiles, int group,
+                          int* per_cu) {
   if (attn_has_mfma_instance(bf16, d, block)) {
     const int threads = 2 * block;
-#define FV_OCC(D, B)                                                                       \
-  if (d == D && block == B)                                                                \
-    return v_tiles ? occupancy_of(attn_mfma_dma_kernel<D, B, true>, threads, per_cu)       \
-                   : occupancy_of(attn_mfma_kernel<D, B, true>, threads, per_cu);
+#define FV_OCC(D, B)                                                                          \
+  if (d == D && block == B) {                                                                 \
+    if (v_tiles && group == 2)                                                                \
+      return occupancy_of(attn_mfma_pair_kernel<D, B, true>, 2 * threads, per_cu);            \
+    return v_tiles ? occupancy_of(attn_mfma_dma_kernel<D, B, true>, threads, per_cu)          \
+                   : occupancy_of(attn_mfma_kernel<D, B, true>, threads, per_cu);             \
+  }
     FV_OCC(128, 128)
     FV_OCC(64, 64)
     FV_OCC(64, 128)
@@ -788,6 +1115,12 @@ bool attn_has_mfma_instance(bool bf16, int d, int block) {
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, bool bf16, hipStream_t s) {
+  if (attn_has_mfma_instance(bf16, a.d, a.block) && a.v_tiles && a.group == 2) {
+    if (a.d == 128 && a.block == 128) return launch_mfma_pair<128, 128>(a, s);
+    if (a.d == 64 && a.block == 64) return launch_mfma_pair<64, 64>(a, s);
+    if (a.d == 64 && a.block == 128) return launch_mfma_pair<64, 128>(a, s);
+    return launch_mfma_pair<128, 64>(a, s);
+  }
   if (attn_has_mfma_instance(bf16, a.d, a.block) && a.v_tiles) {
     if (a.d == 128 && a.block == 128) return launch_mfma_dma<128, 128>(a, s);
     if (a.d == 64 && a.block == 64) return launch_mfma_dma<64, 64>(a, s);

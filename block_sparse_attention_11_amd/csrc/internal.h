@@ -14,6 +14,10 @@ struct bf16s {
   uint16_t bits;
 };
 
+// V^T tile layout (fvattn_pack_v): 8-byte unit u of tile row c is stored at
+// unit position u ^ vt_unit_swap(c).
+__host__ __device__ inline int vt_unit_swap(int c) { return ((c >> 3) ^ (c >> 4)) & 1; }
+
 // ---- hilbert.hip -----------------------------------------------------------
 hipError_t launch_hilbert(int T, int Y, int X, int32_t* perm, int32_t* inv,
                           hipStream_t s);
@@ -22,7 +26,7 @@ hipError_t launch_hilbert(int T, int Y, int X, int32_t* perm, int32_t* inv,
 hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* index,
                                int heads, int n, size_t row_bytes,
                                hipStream_t s);
-// bf16 only; requires block % 4 == 0 and d % 8 == 0
+// bf16 only; requires block % 8 == 0 and d % 8 == 0
 hipError_t launch_pack_v(const void* src, void* dst, const int32_t* index, int heads,
                          int n, int d, int block, hipStream_t s);
 
@@ -42,12 +46,13 @@ hipError_t launch_route(const void* q, const void* k, bool bf16, int heads,
 
 // ---- schedule.hip ----------------------------------------------------------
 constexpr int kMaxWorkers = 2048;
-constexpr int kMaxCost = 16383;
+constexpr int kMaxCost = 65535;
 size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers);
-hipError_t launch_schedule(const int32_t* kv_count, int tiles, int n_workers,
-                           bool tile_order, int32_t* lpt_order, int32_t* worker_offsets,
-                           int32_t* worker_tiles, int64_t* worker_load, void* ws,
-                           hipStream_t s);
+// tiles = heads * ceil(n_qblocks / group); tile t = h * ceil(nq/group) + m
+hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group,
+                           int n_workers, bool tile_order, int32_t* lpt_order,
+                           int32_t* worker_offsets, int32_t* worker_tiles,
+                           int64_t* worker_load, void* ws, hipStream_t s);
 
 // ---- attn.hip --------------------------------------------------------------
 struct AttnArgs {
@@ -64,10 +69,13 @@ struct AttnArgs {
   int n_workers;
   uint64_t* timing;               // null or [n_workers][4]
   bool v_tiles;                   // V as [heads][nb][d][block] transposed tiles
+  int group;                      // q-blocks per tile (1 or 2)
+  int tiles_per_head;             // ceil(nb / group)
 };
 bool attn_has_mfma_instance(bool bf16, int d, int block);
 // resident persistent workgroups per CU of the kernel that would run
-hipError_t attn_occupancy(bool bf16, int d, int block, bool v_tiles, int* per_cu);
+hipError_t attn_occupancy(bool bf16, int d, int block, bool v_tiles, int group,
+                          int* per_cu);
 hipError_t launch_sparse_attn(const AttnArgs& a, bool bf16, hipStream_t s);
 
 }  // namespace fvattn

@@ -51,12 +51,16 @@ hipError_t launch_typed(const void* src, void* dst, const int32_t* index,
   return hipGetLastError();
 }
 
-// dst[h][j][c][key] = src[h][index[j*block + key]][c] for key < rows of block j,
-// 0 for the padding keys of the last block: V in Hilbert order, stored as one
-// transposed [d][block] tile per key block.  A thread moves a 4-key x 8-column
-// unit: four 16-byte row loads, eight 8-byte stores (byte shuffles with
-// v_perm_b32); lanes are laid out key-group fastest so that each group of 32
-// lanes writes 256 contiguous bytes of one tile row.
+// V in Hilbert order as one transposed [d][block] tile per key block:
+//   tile row c holds column c of the block's rows (padding keys are 0), in
+//   8-byte units of 4 keys; unit u of row c is stored at position
+//   u ^ vt_unit_swap(c), which swaps the two halves of every 16-byte group on
+//   rows where bit 3 xor bit 4 of c is set.  The attention kernel reads 8 bytes
+//   per lane from 32 consecutive tile rows at a time; the swap puts rows c and
+//   c+16 (and c, c+8) on different LDS banks.
+// A thread moves a 4-key x 8-column unit: four 16-byte row loads, eight 8-byte
+// stores (byte shuffles with v_perm_b32); lanes run key-group fastest so 32
+// lanes write 256 contiguous bytes of one tile row.
 __global__ __launch_bounds__(kPermuteThreads) void pack_v_kernel(
     const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
     const int32_t* __restrict__ index, int n, int d, int block, int nb) {
@@ -87,7 +91,8 @@ __global__ __launch_bounds__(kPermuteThreads) void pack_v_kernel(
     uint2 o;
     o.x = __builtin_amdgcn_perm(w1, w0, sel);
     o.y = __builtin_amdgcn_perm(w3, w2, sel);
-    *reinterpret_cast<uint2*>(tile + (size_t)(8 * c8 + dd) * block + 4 * kq) = o;
+    const int row = 8 * c8 + dd;
+    *reinterpret_cast<uint2*>(tile + (size_t)row * block + 4 * (kq ^ vt_unit_swap(row))) = o;
   }
 }
 

@@ -1,6 +1,10 @@
 // LPT work list over (head, q-block) tiles for the persistent attention
 // kernel.
 //
+// A tile is `group` consecutive q-blocks of one head (1 or 2; the attention
+// kernel that shares K/V tiles between two q-blocks works on pairs); its cost
+// is the sum of their kept-block counts.
+//
 // Source of the problem: after the mask exists every head's load in sparse
 // blocks is known, and a few heavy heads set the critical path (aixai.ru
 // FVAttn post, "Runtime Load Balancing (RLB)").  On one GPU the balanced
@@ -46,6 +50,7 @@ struct SchedWs {
   int32_t* owner;   // worker of the k-th tile in LPT order
   int32_t* slot;    // its position in that worker's list
   int32_t* owner_by_tile;  // worker of tile t
+  int32_t* group_cost;     // per-tile cost when a tile spans several q-blocks
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -58,7 +63,8 @@ SchedWs carve(void* ws, int tiles) {
                  reinterpret_cast<int32_t*>(b + 3 * one),
                  reinterpret_cast<int32_t*>(b + 4 * one),
                  reinterpret_cast<int32_t*>(b + 5 * one),
-                 reinterpret_cast<int32_t*>(b + 6 * one)};
+                 reinterpret_cast<int32_t*>(b + 6 * one),
+                 reinterpret_cast<int32_t*>(b + 7 * one)};
 }
 
 __device__ inline int clamp_cost(int c) { return min(max(c, 0), kMaxCost); }
@@ -273,6 +279,19 @@ __global__ __launch_bounds__(kAssignThreads) void lpt_assign_kernel(
   }
 }
 
+// cost of tile t = (h, m) covering q-blocks [m*group, min(nq, (m+1)*group))
+__global__ __launch_bounds__(256) void group_cost_kernel(
+    const int32_t* __restrict__ kv_count, int nq, int group, int tiles_per_head,
+    int tiles, int32_t* __restrict__ out) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= tiles) return;
+  const int h = t / tiles_per_head, m = t - h * tiles_per_head;
+  int c = 0;
+  for (int i = m * group; i < min(nq, (m + 1) * group); ++i)
+    c += min(max(kv_count[(size_t)h * nq + i], 0), kMaxCost);
+  out[t] = min(c, kMaxCost);
+}
+
 __global__ __launch_bounds__(256) void lpt_scatter_kernel(
     const int32_t* __restrict__ lpt_order, int tiles, SchedWs ws,
     const int32_t* __restrict__ worker_offsets, int32_t* __restrict__ worker_tiles) {
@@ -285,24 +304,34 @@ __global__ __launch_bounds__(256) void lpt_scatter_kernel(
 size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers) {
   (void)n_workers;
   const size_t tiles = (size_t)heads * n_qblocks;
-  return 7 * align_up(sizeof(int32_t) * tiles, 256);
+  return 8 * align_up(sizeof(int32_t) * tiles, 256);
 }
 
-hipError_t launch_schedule(const int32_t* kv_count, int tiles, int n_workers,
-                           bool tile_order, int32_t* lpt_order, int32_t* worker_offsets,
-                           int32_t* worker_tiles, int64_t* worker_load, void* wsp,
-                           hipStream_t s) {
-  SchedWs ws = carve(wsp, tiles);
-  hipLaunchKernelGGL(lpt_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, kv_count,
+hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group,
+                           int n_workers, bool tile_order, int32_t* lpt_order,
+                           int32_t* worker_offsets, int32_t* worker_tiles,
+                           int64_t* worker_load, void* wsp, hipStream_t s) {
+  const int per_head = (n_qblocks + group - 1) / group;
+  const int tiles = heads * per_head;
+  SchedWs ws = carve(wsp, heads * n_qblocks);
+  const int32_t* cost = kv_count;
+  if (group > 1) {
+    hipLaunchKernelGGL(group_cost_kernel, dim3((tiles + 255) / 256), dim3(256), 0, s,
+                       kv_count, n_qblocks, group, per_head, tiles, ws.group_cost);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+    cost = ws.group_cost;
+  }
+  hipLaunchKernelGGL(lpt_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, cost,
                      tiles, ws, lpt_order, false);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lpt_assign_kernel, dim3(1), dim3(kAssignThreads), 0, s, kv_count,
+  hipLaunchKernelGGL(lpt_assign_kernel, dim3(1), dim3(kAssignThreads), 0, s, cost,
                      lpt_order, tiles, n_workers, ws, worker_offsets, worker_load);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (tile_order) {
-    hipLaunchKernelGGL(lpt_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, kv_count,
+    hipLaunchKernelGGL(lpt_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, cost,
                        tiles, ws, worker_tiles, true);
   } else {
     hipLaunchKernelGGL(lpt_scatter_kernel, dim3((tiles + 255) / 256), dim3(256), 0, s,

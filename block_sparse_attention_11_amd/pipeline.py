@@ -30,7 +30,7 @@ def default_workers(device=None) -> int:
 class FVAttnPath:
     def __init__(self, heads: int, grid, d: int, block: int, dtype=torch.bfloat16,
                  n_workers: int | None = None, device="cuda", tile_order: bool = True,
-                 v_tiles: bool | None = None):
+                 v_tiles: bool | None = None, group: int | None = None):
         self.heads, self.grid, self.d, self.block = heads, tuple(grid), d, block
         T, Y, X = self.grid
         self.n = T * Y * X
@@ -43,16 +43,19 @@ class FVAttnPath:
         self.perm = torch.empty(n, **i32)
         self.inv_perm = torch.empty(n, **i32)
         # V goes to transposed key-block tiles when the bf16 tile packer applies
-        can_tile = dtype == torch.bfloat16 and d % 8 == 0 and block % 4 == 0
+        can_tile = dtype == torch.bfloat16 and d % 8 == 0 and block % 8 == 0
         self.v_tiles = can_tile if v_tiles is None else (v_tiles and can_tile)
         self.qh = torch.empty((H, n, d), dtype=dtype, device=dev)
         self.kh = torch.empty_like(self.qh)
         self.vh = (torch.empty((H, nb, d, block), dtype=dtype, device=dev) if self.v_tiles
                    else torch.empty_like(self.qh))
         self.oh = torch.empty_like(self.qh)
+        # tiles of two q-blocks share each K/V block load (tiled V only)
+        self.group = (2 if self.v_tiles else 1) if group is None else group
+        self.tiles = H * ((nb + self.group - 1) // self.group)
         with torch.cuda.device(dev):
-            self.n_workers = n_workers or min(MAX_WORKERS,
-                                              _lib.attn_workers(dtype, d, block, self.v_tiles))
+            self.n_workers = n_workers or min(
+                MAX_WORKERS, _lib.attn_workers(dtype, d, block, self.v_tiles, self.group))
         self.mask = torch.empty((H, nb, nb), dtype=torch.uint8, device=dev)
         self.kv_count = torch.empty((H, nb), **i32)
         self.kv_index = torch.empty((H, nb, nb), **i32)
@@ -61,9 +64,9 @@ class FVAttnPath:
         self.route_ws = torch.empty(_lib.route_workspace_size(H, n, d, block),
                                     dtype=torch.uint8, device=dev)
         W = self.n_workers
-        self.lpt_order = torch.empty(H * nb, **i32)
+        self.lpt_order = torch.empty(self.tiles, **i32)
         self.worker_offsets = torch.empty(W + 1, **i32)
-        self.worker_tiles = torch.empty(H * nb, **i32)
+        self.worker_tiles = torch.empty(self.tiles, **i32)
         self.worker_load = torch.empty(W, dtype=torch.int64, device=dev)
         self.sched_ws = torch.empty(_lib.schedule_workspace_size(H, nb, W),
                                     dtype=torch.uint8, device=dev)
@@ -90,17 +93,19 @@ class FVAttnPath:
     def schedule(self):
         _lib.schedule(self.kv_count, self.n_workers, self.lpt_order, self.worker_offsets,
                       self.worker_tiles, self.worker_load, self.sched_ws,
-                      tile_order=self.tile_order)
+                      tile_order=self.tile_order, group=self.group)
 
     def attend(self, balanced: bool = True, timing: bool = True):
         if balanced:
             _lib.sparse_attn(self.qh, self.kh, self.vh, self.oh, self.block,
                              self.kv_count, self.kv_index, self.worker_offsets,
                              self.worker_tiles, self.n_workers,
-                             self.timing if timing else None, v_tiles=self.v_tiles)
+                             self.timing if timing else None, v_tiles=self.v_tiles,
+                             group=self.group)
         else:
             _lib.sparse_attn(self.qh, self.kh, self.vh, self.oh, self.block,
-                             self.kv_count, self.kv_index, v_tiles=self.v_tiles)
+                             self.kv_count, self.kv_index, v_tiles=self.v_tiles,
+                             group=self.group)
 
     def to_tokens(self, out):
         _lib.permute_rows(self.oh, out, self.inv_perm)

@@ -97,14 +97,18 @@ int fvattn_permute_rows(const void* src, void* dst, const int32_t* index,
                         hipStream_t stream);
 
 /*
- * Row gather into transposed key-block tiles, used for V:
- *   dst[h][j][c][r] = src[h][index[j*block + r]][c]   for j*block + r < n,
- *   dst[h][j][c][r] = 0                               for the padding rows
- *                                                     of the last block.
- * dst holds heads * nB * d * block elements (FVATTN_V_TILES layout).  The
- * attention kernels read V^T as the A operand of the P.V product; producing
- * it inside the Hilbert gather costs no extra memory traffic.
- * bf16 only; block % 4 == 0, d % 8 == 0 (else FVATTN_EUNSUPPORTED).
+ * Row gather into transposed key-block tiles, used for V (FVATTN_V_TILES):
+ *   tile (h, j) row c holds column c of rows index[j*block + r] of src[h],
+ *   r = 0 .. block-1, with 0 for the padding rows of the last block.  Each
+ *   tile row is stored in 8-byte units of 4 consecutive r; unit u sits at unit
+ *   position u ^ (((c >> 3) ^ (c >> 4)) & 1), a swap of the two halves of
+ *   every 16-byte group on some rows that keeps the attention kernel's LDS
+ *   reads free of bank conflicts.  So element (h, j, c, r) is at
+ *   ((h*nB + j)*d + c)*block + 4*((r/4) ^ s(c)) + r%4.
+ * dst holds heads * nB * d * block elements.  The attention kernels read
+ * V^T as the A operand of the P.V product; producing it inside the Hilbert
+ * gather costs no extra memory traffic.
+ * bf16 only; block % 8 == 0, d % 8 == 0 (else FVATTN_EUNSUPPORTED).
  */
 int fvattn_pack_v(const void* src, void* dst, const int32_t* index, int heads,
                   int n, int d, int block, int dtype, hipStream_t stream);
@@ -146,21 +150,24 @@ int fvattn_route(const void* q, const void* k, int dtype, int heads, int n,
                  hipStream_t stream);
 
 /*
- * LPT work list over (head, q-block) tiles for n_workers persistent
- * workgroups.
+ * LPT work list over tiles for n_workers persistent workgroups.  A tile is
+ * `group` consecutive q-blocks of one head (group 1 or 2): tile
+ * t = h * ceil(n_qblocks / group) + m covers q-blocks [m*group,
+ * min(n_qblocks, (m+1)*group)).  group 2 matches the attention kernel that
+ * loads each K/V block once for two q-blocks.
  *
  * Source: once the mask exists each head's load in sparse blocks is known
  * exactly and a few heavy heads set the critical path (aixai.ru FVAttn post,
  * section "Runtime Load Balancing (RLB)").  On one GPU the balanced resource
  * is the set of workgroups; the rule is Graham's LPT:
- *   cost(t) = kv_count[t] (t = h*n_qblocks + i);
+ *   cost(t) = sum of kv_count over the tile's q-blocks;
  *   lpt_order = tiles sorted by (cost descending, t ascending);
  *   in that order each tile goes to the worker with the least load so far
  *   (lowest worker index on ties) and is appended to its list.
- * Outputs (device):
- *   lpt_order      int32 [heads*n_qblocks];
+ * Outputs (device), with tiles = heads * ceil(n_qblocks / group):
+ *   lpt_order      int32 [tiles];
  *   worker_offsets int32 [n_workers+1], exclusive prefix of list sizes;
- *   worker_tiles   int32 [heads*n_qblocks], the lists concatenated;
+ *   worker_tiles   int32 [tiles], the lists concatenated;
  *   worker_load    int64 [n_workers], summed cost per worker.
  * flags:
  *   0                        each list in assignment order;
@@ -169,12 +176,13 @@ int fvattn_route(const void* q, const void* k, int dtype, int heads, int n,
  *                            walks heads in step across workgroups, so K/V
  *                            blocks are shared in L2 while they run.
  * Bit-exact: there is exactly one correct result per input and flag.
- * Limits: 1 <= n_workers <= 2048; costs in [0, 65535]; heads*n_qblocks < 2^31.
+ * Limits: 1 <= n_workers <= 2048; tile costs are clamped to [0, 65535];
+ * heads*n_qblocks < 2^31; group in {1, 2} (else FVATTN_EINVAL).
  * workspace: at least fvattn_schedule_workspace_size() bytes.
  */
 size_t fvattn_schedule_workspace_size(int heads, int n_qblocks, int n_workers);
 int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
-                    int n_workers, int flags, int32_t* lpt_order,
+                    int group, int n_workers, int flags, int32_t* lpt_order,
                     int32_t* worker_offsets, int32_t* worker_tiles,
                     int64_t* worker_load, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
@@ -193,10 +201,12 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
  * scale <= 0 selects 1/sqrt(d).
  * v_layout: FVATTN_V_ROWS or FVATTN_V_TILES (see fvattn_pack_v); Q, K and O
  * are always [heads][n][d].  With FVATTN_V_TILES the V tiles must fit in 2 GiB
- * (else FVATTN_EUNSUPPORTED).
+ * and block % 8 == 0 (else FVATTN_EUNSUPPORTED).
  * kv_index entries must lie in [0, nB): the MFMA kernels clamp others into
  * that range, the plain kernel skips them (memory-safe, result undefined).
- * Work distribution:
+ * Work distribution (tiles of `group` q-blocks, numbered as in
+ * fvattn_schedule; group 2 with FVATTN_V_TILES and an MFMA shape runs the
+ * kernel that shares each K/V block between the two q-blocks):
  *   worker_offsets != NULL: persistent launch of n_workers workgroups;
  *     workgroup w runs the tiles worker_tiles[worker_offsets[w] ..
  *     worker_offsets[w+1]) in order (the LPT lists of fvattn_schedule);
@@ -212,7 +222,8 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
  */
 int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o,
                        int dtype, int heads, int n, int d, int block,
-                       int v_layout, float scale, const int32_t* kv_count,
+                       int v_layout, int group, float scale,
+                       const int32_t* kv_count,
                        const int32_t* kv_index, const int32_t* worker_offsets,
                        const int32_t* worker_tiles, int n_workers,
                        uint64_t* timing, hipStream_t stream);
@@ -220,13 +231,14 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o,
 /*
  * Persistent workers for fvattn_sparse_attn on the current device: the
  * number of workgroups of the attention kernel that (dtype, d, block,
- * v_layout) selects which can be resident at once (compute units times
+ * v_layout, group) selects which can be resident at once (compute units times
  * workgroups per compute unit).  Pass it as n_workers to fvattn_schedule and
  * fvattn_sparse_attn so every compute unit stays busy.  Writes *workers;
  * returns FVATTN_EINVAL for bad arguments and FVATTN_ELAUNCH if the HIP
  * runtime query fails (for instance with no GPU).
  */
-int fvattn_attn_workers(int dtype, int d, int block, int v_layout, int* workers);
+int fvattn_attn_workers(int dtype, int d, int block, int v_layout, int group,
+                        int* workers);
 
 #ifdef __cplusplus
 }

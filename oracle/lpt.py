@@ -63,3 +63,15 @@ def lpt_schedule(costs: np.ndarray, n_workers: int, tile_order: bool = False):
 def predicted_imbalance(loads: np.ndarray) -> float:
     loads = np.asarray(loads, dtype=np.float64)
     return float(loads.max() / loads.mean()) if loads.mean() > 0 else 1.0
+
+
+def group_costs(kv_count, group: int) -> np.ndarray:
+    """Cost of each tile of `group` consecutive q-blocks of one head: the sum
+    of their kept-block counts.  kv_count [H, nB] -> [H * ceil(nB / group)]."""
+    kv = np.asarray(kv_count, dtype=np.int64)
+    H, nb = kv.shape
+    per = (nb + group - 1) // group
+    out = np.zeros((H, per), dtype=np.int64)
+    for m in range(per):
+        out[:, m] = kv[:, m * group:min(nb, (m + 1) * group)].sum(axis=1)
+    return out.reshape(-1)

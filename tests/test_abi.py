@@ -51,7 +51,7 @@ def test_workspace_sizes():
     rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert lib.fvattn_route_workspace_size(40, 75600, 128, 128) == 2 * rnd(pooled) + rnd(scores)
     assert lib.fvattn_route_workspace_size(0, 75600, 128, 128) == 0
-    assert lib.fvattn_schedule_workspace_size(40, 591, 256) == 7 * rnd(40 * 591 * 4)
+    assert lib.fvattn_schedule_workspace_size(40, 591, 256) == 8 * rnd(40 * 591 * 4)
     assert lib.fvattn_schedule_workspace_size(40, 591, 0) == 0
 
 
@@ -82,28 +82,33 @@ def _validation_main():
         (lib.fvattn_route(P, P, 1, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, N, 1 << 30, N), EWS),
         (lib.fvattn_route(P, P, 1, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, P, 16, N), EWS),
         # schedule
-        (lib.fvattn_schedule(P, 40, 591, 2049, 0, P, P, P, P, P, 1 << 30, N), EUNS),
-        (lib.fvattn_schedule(P, 40, 591, 256, 2, P, P, P, P, P, 1 << 30, N), EINVAL),
-        (lib.fvattn_schedule(P, 40, 591, 0, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
-        (lib.fvattn_schedule(N, 40, 591, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
-        (lib.fvattn_schedule(P, 40, 591, 256, 1, P, P, P, P, P, 100, N), EWS),
+        (lib.fvattn_schedule(P, 40, 591, 1, 2049, 0, P, P, P, P, P, 1 << 30, N), EUNS),
+        (lib.fvattn_schedule(P, 40, 591, 1, 256, 2, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule(P, 40, 591, 1, 0, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule(N, 40, 591, 1, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule(P, 40, 591, 1, 256, 1, P, P, P, P, P, 100, N), EWS),
         # attention
-        (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 0.0, P, P, N, N, 0, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 0.0, P, P, N, N, 0, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 256, 16, 0, 0.0, P, P, N, N, 0, N, N), EUNS),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, float("inf"), P, P, N, N, 0, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 0.0, P, P, P, N, 4, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 0.0, P, P, P, P, 0, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 0.0, P, P, N, N, 0, P, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 2, 0.0, P, P, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 256, 16, 0, 1, 0.0, P, P, N, N, 0, N, N), EUNS),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, float("inf"), P, P, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, N, 4, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, P, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, P, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 2, 1, 0.0, P, P, N, N, 0, N, N), EINVAL),
         # workers
-        (lib.fvattn_attn_workers(1, 128, 128, 1, N), EINVAL),
-        (lib.fvattn_attn_workers(1, 128, 128, 5, ctypes.byref(ctypes.c_int())), EINVAL),
+        (lib.fvattn_attn_workers(1, 128, 128, 1, 2, N), EINVAL),
+        (lib.fvattn_attn_workers(1, 128, 128, 1, 3, ctypes.byref(ctypes.c_int())), EINVAL),
+        (lib.fvattn_attn_workers(1, 128, 128, 5, 1, ctypes.byref(ctypes.c_int())), EINVAL),
+        (lib.fvattn_schedule(P, 40, 591, 3, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 1, 3, 0.0, P, P, N, N, 0, N, N), EINVAL),
         # pack_v
         (lib.fvattn_pack_v(P, P, P, 1, 128, 64, 16, 1, N), EINVAL),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 16, 0, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 60, 16, 1, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 18, 1, N), EUNS),
+        (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 12, 1, N), EUNS),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 12, 1, 1, 0.0, P, P, N, N, 0, N, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), N, 1, 128, 64, 16, 1, N), EINVAL),
     ]
     bad = [(i, got, want) for i, (got, want) in enumerate(checks) if got != want]

@@ -75,7 +75,7 @@ def test_permute_rows_bit_exact(dtype, d):
 
 
 @pytest.mark.parametrize("d,block,n", [(128, 128, 75600 // 40), (64, 64, 390), (64, 16, 105),
-                                       (128, 64, 1000), (8, 4, 9)])
+                                       (128, 64, 1000), (8, 8, 9), (16, 24, 50)])
 def test_pack_v_bit_exact(d, block, n):
     say(f"pack_v d={d} block={block} n={n}")
     g = torch.Generator().manual_seed(11)
@@ -89,8 +89,16 @@ def test_pack_v_bit_exact(d, block, n):
     xs = ort.permute_rows(x.view(torch.int16).numpy(), idx.numpy())      # [H, n, d]
     pad = np.zeros((H, nb * block, d), dtype=np.int16)
     pad[:, :n] = xs
-    ref = pad.reshape(H, nb, block, d).transpose(0, 1, 3, 2)
-    assert np.array_equal(dst.cpu().view(torch.int16).numpy(), ref)
+    ref = pad.reshape(H, nb, block, d).transpose(0, 1, 3, 2)          # [H, nb, d, block]
+    # unit (4 keys) u of tile row c sits at u ^ s(c), s(c) = bit3(c) ^ bit4(c)
+    units = ref.reshape(H, nb, d, block // 4, 4)
+    swapped = np.empty_like(units)
+    for c in range(d):
+        sw = ((c >> 3) ^ (c >> 4)) & 1
+        u = np.arange(block // 4)
+        swapped[:, :, c, u ^ sw] = units[:, :, c, u]
+    assert np.array_equal(dst.cpu().view(torch.int16).numpy(),
+                          swapped.reshape(H, nb, d, block))
 
 
 # ---------------------------------------------------------------------------
@@ -176,16 +184,16 @@ def test_route_parity(name, p, kf):
 # ---------------------------------------------------------------------------
 # LPT schedule
 # ---------------------------------------------------------------------------
-def gpu_schedule(costs_2d, W, tile_order=False):
+def gpu_schedule(costs_2d, W, tile_order=False, group=1):
     H, nb = costs_2d.shape
     kvc = torch.from_numpy(costs_2d.astype(np.int32)).to(DEV)
-    tiles = H * nb
+    tiles = H * ((nb + group - 1) // group)
     order = torch.empty(tiles, dtype=torch.int32, device=DEV)
     off = torch.empty(W + 1, dtype=torch.int32, device=DEV)
     wt = torch.empty(tiles, dtype=torch.int32, device=DEV)
     wl = torch.empty(W, dtype=torch.int64, device=DEV)
     ws = torch.empty(_lib.schedule_workspace_size(H, nb, W), dtype=torch.uint8, device=DEV)
-    _lib.schedule(kvc, W, order, off, wt, wl, ws, tile_order=tile_order)
+    _lib.schedule(kvc, W, order, off, wt, wl, ws, tile_order=tile_order, group=group)
     torch.cuda.synchronize()
     return order.cpu().numpy(), off.cpu().numpy(), wt.cpu().numpy(), wl.cpu().numpy()
 
@@ -204,10 +212,11 @@ SCHED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("group", [1, 2])
 @pytest.mark.parametrize("tile_order", [False, True])
 @pytest.mark.parametrize("name,costs,W", SCHED_CASES)
-def test_schedule_bit_exact(name, costs, W, tile_order):
-    say(f"schedule {name} W={W} tile_order={tile_order}")
+def test_schedule_bit_exact(name, costs, W, tile_order, group):
+    say(f"schedule {name} W={W} tile_order={tile_order} group={group}")
     rng = np.random.default_rng(sum(map(ord, name)))
     if name == "random_ties":
         costs = rng.integers(1, 9, size=(8, 37))
@@ -217,8 +226,8 @@ def test_schedule_bit_exact(name, costs, W, tile_order):
         costs = rng.integers(8, 1155, size=(40, 1154))
     elif name == "big_costs":
         costs = rng.integers(0, 16384, size=(5, 333))
-    got = gpu_schedule(costs, W, tile_order)
-    ref = olpt.lpt_schedule(costs.reshape(-1), W, tile_order=tile_order)
+    got = gpu_schedule(costs, W, tile_order, group)
+    ref = olpt.lpt_schedule(olpt.group_costs(costs, group), W, tile_order=tile_order)
     for g, r, what in zip(got, ref, ("order", "offsets", "tiles", "loads")):
         assert np.array_equal(g, r), what
 
@@ -231,13 +240,13 @@ ATTN_CASES = ["tiny", "small", "ragged_f32", "ragged_bf16", "mid_bf16", "mid_bf1
 
 @pytest.mark.parametrize("name", ATTN_CASES)
 @pytest.mark.parametrize("balanced", [True, False])
-@pytest.mark.parametrize("v_tiles", [True, False])
-def test_attention_parity(name, balanced, v_tiles):
+@pytest.mark.parametrize("v_tiles,group", [(True, 2), (True, 1), (False, 1), (False, 2)])
+def test_attention_parity(name, balanced, v_tiles, group):
     w = workload(name)
-    say(f"attention {name} balanced={balanced} v_tiles={v_tiles}")
+    say(f"attention {name} balanced={balanced} v_tiles={v_tiles} group={group}")
     q, k, v, _ = synth.make_inputs(w, "cpu")
     path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, n_workers=7,
-                      device=DEV, v_tiles=v_tiles)
+                      device=DEV, v_tiles=v_tiles, group=group)
     out = path.run(q.to(DEV), k.to(DEV), v.to(DEV), w.p, w.k, balanced=balanced)
     torch.cuda.synchronize()
     perm = path.perm.cpu().numpy()
@@ -272,7 +281,7 @@ def test_dense_control_matches_brute_force(name):
     assert err["max_abs"] <= tol["max_abs"] and err["rel_l2"] <= tol["rel_l2"], err
 
 
-def attn_call(q, k, v, o, block, cnt, idx, v_tiles, **kw):
+def attn_call(q, k, v, o, block, cnt, idx, v_tiles, group=1, **kw):
     """sparse_attn with V given as rows or packed into tiles (identity order)."""
     if v_tiles:
         H, n, d = v.shape
@@ -280,19 +289,18 @@ def attn_call(q, k, v, o, block, cnt, idx, v_tiles, **kw):
         vt = torch.empty((H, nb, d, block), dtype=v.dtype, device=DEV)
         _lib.pack_v(v, vt, torch.arange(n, dtype=torch.int32, device=DEV), block)
         v = vt
-    _lib.sparse_attn(q, k, v, o, block, cnt, idx, v_tiles=v_tiles, **kw)
+    _lib.sparse_attn(q, k, v, o, block, cnt, idx, v_tiles=v_tiles, group=group, **kw)
 
 
-@pytest.mark.parametrize("dtype,d,block,v_tiles", [(torch.bfloat16, 128, 128, True),
-                                                   (torch.bfloat16, 128, 128, False),
-                                                   (torch.bfloat16, 64, 64, True),
-                                                   (torch.bfloat16, 64, 64, False),
-                                                   (torch.bfloat16, 64, 16, True),
-                                                   (torch.float32, 64, 16, False)])
-def test_attention_handmade_lists(dtype, d, block, v_tiles):
+@pytest.mark.parametrize("dtype,d,block,v_tiles,group", [
+    (torch.bfloat16, 128, 128, True, 2), (torch.bfloat16, 128, 128, True, 1),
+    (torch.bfloat16, 128, 128, False, 1), (torch.bfloat16, 64, 64, True, 2),
+    (torch.bfloat16, 64, 64, False, 2), (torch.bfloat16, 64, 16, True, 1),
+    (torch.float32, 64, 16, False, 2)])
+def test_attention_handmade_lists(dtype, d, block, v_tiles, group):
     """Edge cases: an empty row (written as zeros), a single kept block, only
-    the short tail block, and constant V rows."""
-    say(f"handmade lists {dtype} d={d} block={block} v_tiles={v_tiles}")
+    the short tail block, a pair whose two lists differ, and constant V."""
+    say(f"handmade lists {dtype} d={d} block={block} v_tiles={v_tiles} group={group}")
     H, n = 2, 3 * block + block // 2 + 1
     nb = 4
     g = torch.Generator().manual_seed(3)
@@ -310,7 +318,7 @@ def test_attention_handmade_lists(dtype, d, block, v_tiles):
     idx[1, 3, 0] = 3
     o = torch.full((H, n, d), float("nan"), dtype=dtype, device=DEV)
     attn_call(q.to(DEV), k.to(DEV), v.to(DEV), o, block,
-              torch.from_numpy(cnt).to(DEV), torch.from_numpy(idx).to(DEV), v_tiles)
+              torch.from_numpy(cnt).to(DEV), torch.from_numpy(idx).to(DEV), v_tiles, group)
     torch.cuda.synchronize()
     got = to_np(o)
     qq, kk, vv = (to_np(x).astype(np.float64) for x in (q, k, v))
@@ -324,7 +332,7 @@ def test_attention_handmade_lists(dtype, d, block, v_tiles):
     # constant V rows give the constant, whatever the mask
     vc = torch.arange(d, dtype=torch.float32).div(d).expand(H, n, d).contiguous().to(dtype)
     attn_call(q.to(DEV), k.to(DEV), vc.to(DEV), o, block,
-              torch.from_numpy(cnt).to(DEV), torch.from_numpy(idx).to(DEV), v_tiles)
+              torch.from_numpy(cnt).to(DEV), torch.from_numpy(idx).to(DEV), v_tiles, group)
     torch.cuda.synchronize()
     got = to_np(o)
     exp = to_np(vc)
@@ -373,6 +381,7 @@ def test_attn_workers_is_a_multiple_of_the_cus():
     say("attn_workers")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for v_tiles in (True, False):
-        w = _lib.attn_workers(torch.bfloat16, 128, 128, v_tiles)
-        assert w >= cus and w % cus == 0
+        for group in (1, 2):
+            w = _lib.attn_workers(torch.bfloat16, 128, 128, v_tiles, group)
+            assert w >= cus and w % cus == 0
     assert _lib.attn_workers(torch.float32, 64, 16, False) % cus == 0
