@@ -44,6 +44,20 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def attn_kernel_name(path) -> str:
+    """Name of the attention kernel the library dispatches for this path
+    (same rule as the C ABI: bf16 with d, block in {64, 128} runs on MFMA;
+    V tiles + q-block pairs -> pair kernel, V tiles alone -> DMA kernel)."""
+    mfma = path.dtype == torch.bfloat16 and path.d in (64, 128) and path.block in (64, 128)
+    if not mfma:
+        return f"attn_simple_kernel<{path.d},persistent>"
+    if path.v_tiles and path.group == 2:
+        return f"attn_mfma_pair_kernel<{path.d},{path.block},persistent>"
+    if path.v_tiles:
+        return f"attn_mfma_dma_kernel<{path.d},{path.block},persistent>"
+    return f"attn_mfma_kernel<{path.d},{path.block},persistent>"
+
+
 def kept_flops(path: FVAttnPath) -> float:
     """sum over kept (h, i, j) of 4 * n_i * n_j * d, in float64 on the GPU."""
     nb, blk, n, d = path.nb, path.block, path.n, path.d
@@ -267,7 +281,7 @@ def main():
     res["roofline"] = {"bound": "mfma", "achieved": round(attn_tflops, 2),
                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                        "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                       "traffic": traffic, "kernel": "attn_mfma_kernel<128,128,persistent>"}
+                       "traffic": traffic, "kernel": attn_kernel_name(path)}
 
     if not args.no_controls:
         log("head-major control")
