@@ -63,7 +63,7 @@ int fvattn_pack_v(const void* src, void* dst, const int32_t* index, int heads, i
   if (src == dst) return FVATTN_EINVAL;
   if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
   if (!fits_int32(nblocks(n, block) * block * (long long)d)) return FVATTN_EINVAL;
-  if (dtype != FVATTN_BF16 || block % 8 != 0 || d % 8 != 0) return FVATTN_EUNSUPPORTED;
+  if (dtype != FVATTN_BF16 || block % 16 != 0 || d % 8 != 0) return FVATTN_EUNSUPPORTED;
   if (nblocks(n, block) > 65535) return FVATTN_EUNSUPPORTED;
   return launch_status(fvattn::launch_pack_v(src, dst, index, heads, n, d, block, stream));
 }
@@ -139,7 +139,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   // the tiled-V kernel addresses each tensor with one 32-bit buffer offset;
   // tiles exist only for blocks of a multiple of 8 rows (fvattn_pack_v)
   if (v_layout == FVATTN_V_TILES &&
-      ((long long)heads * nb * block * d * 2 > 0x7fffffffLL || block % 8 != 0))
+      ((long long)heads * nb * block * d * 2 > 0x7fffffffLL || block % 16 != 0))
     return FVATTN_EUNSUPPORTED;
   if (timing && !worker_offsets) return FVATTN_EINVAL;
   fvattn::AttnArgs a;

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kSimpleThreads) void attn_simple_kernel(AttnArgs a)
           Ks[kr][c] = ok ? load_elem(K + (hb + row) * d + c) : 0.f;
           const int kr0 = row - r0;
           const size_t vi = a.v_tiles
-              ? (((size_t)h * nb + j) * d + c) * blk + 4 * ((kr0 >> 2) ^ vt_unit_swap(c)) + (kr0 & 3)
+              ? (((size_t)h * nb + j) * d + c) * blk + vt_pos(kr0)
               : (hb + row) * d + c;
           Vs[kr][c] = ok ? load_elem(V + vi) : 0.f;
         }
@@ -458,10 +458,19 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// V^T tiles in LDS: 16-byte chunk c of row dd sits at chunk position
+// c ^ vt_swz(dd).  A lane of the P.V MFMA reads chunk 2*cb + g of rows
+// 32*dt + col; the XOR term uses the row bits that select 16-byte bank groups
+// inside 256 bytes, so each 16 lanes read 16 distinct bank groups.
+template <int BLK>
+__device__ inline int vt_swz(int dd) {
+  constexpr int CPR = BLK / 8;                  // 16-byte chunks of a V^T row
+  constexpr int RP = BLK >= 128 ? 1 : 128 / BLK; // rows per 256 bytes
+  return (dd / RP) & (CPR - 1);
+}
 template <int D, int BLK>
-__device__ inline uint32_t vt_off(int dd, int chunk, int half) {
-  constexpr int CPR = BLK / 8;    // 16-byte chunks of a V^T row
-  return (uint32_t)(dd * (2 * BLK) + ((chunk ^ (dd & (CPR - 1))) << 4) + half * 8);
+__device__ inline uint32_t vt_off(int dd, int chunk) {
+  return (uint32_t)(dd * (2 * BLK) + ((chunk ^ vt_swz<BLK>(dd)) << 4));
 }
 
 // read-only table entry through the scalar cache (the tables are not written
@@ -489,7 +498,6 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
   const int wave = tid >> 6;
   const int col = lane & 31;
   const int g = lane >> 5;
-  const int vhalf = g ^ vt_unit_swap(col);     // V^T rows 32dt+col share col's bits 3, 4
   const int n = a.n, nb = a.nb;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   uint16_t* O = static_cast<uint16_t*>(a.o);
@@ -514,7 +522,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
   for (int x = 0; x < VDMA; ++x) {
     const int P = (x * NW + wave) * 64 + lane;
     const int dd = P / CPRV, pc = P % CPRV;
-    voff[x] = (uint32_t)(dd * BLK * 2 + (pc ^ (dd & (CPRV - 1))) * 16);
+    voff[x] = (uint32_t)(dd * BLK * 2 + (pc ^ vt_swz<BLK>(dd)) * 16);
   }
   auto dma_k = [&](int h, int j) {
     const uint32_t base = (uint32_t)(((size_t)h * n + (size_t)j * BLK) * D * 2);
@@ -689,9 +697,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int dd = 32 * dt + col;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(Vs + vt_off<D, BLK>(dd, 2 * c, vhalf));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(Vs + vt_off<D, BLK>(dd, 2 * c + 1, vhalf));
-        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+        const u32x4 av = *reinterpret_cast<const u32x4*>(Vs + vt_off<D, BLK>(dd, 2 * c + g));
         acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                             bop, acc_o[dt], 0, 0, 0);
       }
@@ -764,7 +770,6 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   const int wq = wave % (NW / 2);             // 32-query slice inside it
   const int col = lane & 31;
   const int g = lane >> 5;
-  const int vhalf = g ^ vt_unit_swap(col);
   const int n = a.n, nb = a.nb, tph = a.tiles_per_head;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   uint16_t* O = static_cast<uint16_t*>(a.o);
@@ -777,7 +782,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   // DMA instruction x of this wave fills LDS chunks P = (x*NW + wave)*64 + lane;
   // consecutive x advance by NW*64 chunks = a whole number of rows that is a
   // multiple of the swizzle period, so the source offset is affine in x
-  static_assert((NW * 64 / CPRK) % CPRK == 0 && (NW * 64 / CPRV) % CPRV == 0, "swizzle period");
+  static_assert((NW * 64 / CPRK) % CPRK == 0 && (NW * 64 / CPRV) % 16 == 0, "swizzle period");
   constexpr uint32_t kStepK = (NW * 64 / CPRK) * D * 2;     // bytes per DMA step, K
   constexpr uint32_t kStepV = (NW * 64 / CPRV) * BLK * 2;   // and V^T
   uint32_t koff, voff;
@@ -786,7 +791,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
     const int r = P / CPRK, pc = P % CPRK;
     koff = (uint32_t)(r * D * 2 + (pc ^ (r & (CPRK - 1))) * 16);
     const int dd = P / CPRV, pv = P % CPRV;
-    voff = (uint32_t)(dd * BLK * 2 + (pv ^ (dd & (CPRV - 1))) * 16);
+    voff = (uint32_t)(dd * BLK * 2 + (pv ^ vt_swz<BLK>(dd)) * 16);
   }
   auto dma = [&](uint8_t* kb, uint8_t* vb, int h, int j) {
     const uint32_t kbase = (uint32_t)(((size_t)h * n + (size_t)j * BLK) * D * 2);
@@ -985,9 +990,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
             const int dd = 32 * dt + col;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vc + vt_off<D, BLK>(dd, 2 * cb, vhalf));
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vc + vt_off<D, BLK>(dd, 2 * cb + 1, vhalf));
-            const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+            const u32x4 av = *reinterpret_cast<const u32x4*>(vc + vt_off<D, BLK>(dd, 2 * cb + g));
             acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                                 bop, acc_o[dt], 0, 0, 0);
           }

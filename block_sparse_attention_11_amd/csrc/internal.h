@@ -14,9 +14,14 @@ struct bf16s {
   uint16_t bits;
 };
 
-// V^T tile layout (fvattn_pack_v): 8-byte unit u of tile row c is stored at
-// unit position u ^ vt_unit_swap(c).
-__host__ __device__ inline int vt_unit_swap(int c) { return ((c >> 3) ^ (c >> 4)) & 1; }
+// V^T tile layout (fvattn_pack_v): inside each 16-key group of a tile row,
+// the four 4-key units are stored in the order 0, 2, 1, 3, so that keys
+// {4g..4g+3} and {8+4g..8+4g+3} (the keys one lane of a 32x32x16 MFMA holds
+// in the P operand) are 16 contiguous bytes.  Position of key r in its row:
+__host__ __device__ inline int vt_pos(int r) {
+  const int u = (r >> 2) & 3;
+  return (r & ~15) | (((u & 1) << 1 | (u >> 1)) << 2) | (r & 3);
+}
 
 // ---- hilbert.hip -----------------------------------------------------------
 hipError_t launch_hilbert(int T, int Y, int X, int32_t* perm, int32_t* inv,

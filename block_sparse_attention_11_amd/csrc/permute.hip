@@ -53,11 +53,9 @@ hipError_t launch_typed(const void* src, void* dst, const int32_t* index,
 
 // V in Hilbert order as one transposed [d][block] tile per key block:
 //   tile row c holds column c of the block's rows (padding keys are 0), in
-//   8-byte units of 4 keys; unit u of row c is stored at position
-//   u ^ vt_unit_swap(c), which swaps the two halves of every 16-byte group on
-//   rows where bit 3 xor bit 4 of c is set.  The attention kernel reads 8 bytes
-//   per lane from 32 consecutive tile rows at a time; the swap puts rows c and
-//   c+16 (and c, c+8) on different LDS banks.
+//   8-byte units of 4 keys; inside each 16-key group the units are stored in
+//   the order 0, 2, 1, 3 (vt_pos), so the 8 keys one lane of the attention
+//   kernel's P.V MFMA needs are one 16-byte read.
 // A thread moves a 4-key x 8-column unit: four 16-byte row loads, eight 8-byte
 // stores (byte shuffles with v_perm_b32); lanes run key-group fastest so 32
 // lanes write 256 contiguous bytes of one tile row.
@@ -92,7 +90,7 @@ __global__ __launch_bounds__(kPermuteThreads) void pack_v_kernel(
     o.x = __builtin_amdgcn_perm(w1, w0, sel);
     o.y = __builtin_amdgcn_perm(w3, w2, sel);
     const int row = 8 * c8 + dd;
-    *reinterpret_cast<uint2*>(tile + (size_t)row * block + 4 * (kq ^ vt_unit_swap(row))) = o;
+    *reinterpret_cast<uint2*>(tile + (size_t)row * block + vt_pos(4 * kq)) = o;
   }
 }
 

@@ -43,7 +43,7 @@ class FVAttnPath:
         self.perm = torch.empty(n, **i32)
         self.inv_perm = torch.empty(n, **i32)
         # V goes to transposed key-block tiles when the bf16 tile packer applies
-        can_tile = dtype == torch.bfloat16 and d % 8 == 0 and block % 8 == 0
+        can_tile = dtype == torch.bfloat16 and d % 8 == 0 and block % 16 == 0
         self.v_tiles = can_tile if v_tiles is None else (v_tiles and can_tile)
         self.qh = torch.empty((H, n, d), dtype=dtype, device=dev)
         self.kh = torch.empty_like(self.qh)

@@ -100,15 +100,16 @@ int fvattn_permute_rows(const void* src, void* dst, const int32_t* index,
  * Row gather into transposed key-block tiles, used for V (FVATTN_V_TILES):
  *   tile (h, j) row c holds column c of rows index[j*block + r] of src[h],
  *   r = 0 .. block-1, with 0 for the padding rows of the last block.  Each
- *   tile row is stored in 8-byte units of 4 consecutive r; unit u sits at unit
- *   position u ^ (((c >> 3) ^ (c >> 4)) & 1), a swap of the two halves of
- *   every 16-byte group on some rows that keeps the attention kernel's LDS
- *   reads free of bank conflicts.  So element (h, j, c, r) is at
- *   ((h*nB + j)*d + c)*block + 4*((r/4) ^ s(c)) + r%4.
+ *   tile row is stored in 8-byte units of 4 consecutive r; inside every group
+ *   of 16 keys the four units are stored in the order 0, 2, 1, 3, so that the
+ *   8 keys one lane of the attention kernel's 32x32x16 MFMA takes ({4g..4g+3}
+ *   and {8+4g..8+4g+3} of the group, g = 0, 1) are 16 contiguous bytes.  So
+ *   element (h, j, c, r) is at ((h*nB + j)*d + c)*block + pos(r), with
+ *   pos(r) = 16*(r/16) + 4*sigma((r%16)/4) + r%4, sigma = (0, 2, 1, 3).
  * dst holds heads * nB * d * block elements.  The attention kernels read
  * V^T as the A operand of the P.V product; producing it inside the Hilbert
  * gather costs no extra memory traffic.
- * bf16 only; block % 8 == 0, d % 8 == 0 (else FVATTN_EUNSUPPORTED).
+ * bf16 only; block % 16 == 0, d % 8 == 0 (else FVATTN_EUNSUPPORTED).
  */
 int fvattn_pack_v(const void* src, void* dst, const int32_t* index, int heads,
                   int n, int d, int block, int dtype, hipStream_t stream);
@@ -201,7 +202,7 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
  * scale <= 0 selects 1/sqrt(d).
  * v_layout: FVATTN_V_ROWS or FVATTN_V_TILES (see fvattn_pack_v); Q, K and O
  * are always [heads][n][d].  With FVATTN_V_TILES the V tiles must fit in 2 GiB
- * and block % 8 == 0 (else FVATTN_EUNSUPPORTED).
+ * and block % 16 == 0 (else FVATTN_EUNSUPPORTED).
  * kv_index entries must lie in [0, nB): the MFMA kernels clamp others into
  * that range, the plain kernel skips them (memory-safe, result undefined).
  * Work distribution (tiles of `group` q-blocks, numbered as in

@@ -108,6 +108,8 @@ def _validation_main():
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 60, 16, 1, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 18, 1, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 12, 1, N), EUNS),
+        (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 8, 1, N), EUNS),
+        (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 24, 1, N), EUNS),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 12, 1, 1, 0.0, P, P, N, N, 0, N, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), N, 1, 128, 64, 16, 1, N), EINVAL),
     ]

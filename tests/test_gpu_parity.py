@@ -75,7 +75,7 @@ def test_permute_rows_bit_exact(dtype, d):
 
 
 @pytest.mark.parametrize("d,block,n", [(128, 128, 75600 // 40), (64, 64, 390), (64, 16, 105),
-                                       (128, 64, 1000), (8, 8, 9), (16, 24, 50)])
+                                       (128, 64, 1000), (8, 16, 9), (16, 48, 50)])
 def test_pack_v_bit_exact(d, block, n):
     say(f"pack_v d={d} block={block} n={n}")
     g = torch.Generator().manual_seed(11)
@@ -90,15 +90,12 @@ def test_pack_v_bit_exact(d, block, n):
     pad = np.zeros((H, nb * block, d), dtype=np.int16)
     pad[:, :n] = xs
     ref = pad.reshape(H, nb, block, d).transpose(0, 1, 3, 2)          # [H, nb, d, block]
-    # unit (4 keys) u of tile row c sits at u ^ s(c), s(c) = bit3(c) ^ bit4(c)
-    units = ref.reshape(H, nb, d, block // 4, 4)
-    swapped = np.empty_like(units)
-    for c in range(d):
-        sw = ((c >> 3) ^ (c >> 4)) & 1
-        u = np.arange(block // 4)
-        swapped[:, :, c, u ^ sw] = units[:, :, c, u]
+    # inside each 16-key group of a tile row the 4-key units are stored in
+    # the order 0, 2, 1, 3
+    groups = ref.reshape(H, nb, d, block // 16, 4, 4)
+    want = groups[:, :, :, :, [0, 2, 1, 3], :]
     assert np.array_equal(dst.cpu().view(torch.int16).numpy(),
-                          swapped.reshape(H, nb, d, block))
+                          want.reshape(H, nb, d, block))
 
 
 # ---------------------------------------------------------------------------
