@@ -131,7 +131,8 @@ class StageTimer:
         return [x.elapsed_time(y) for x, y in zip(self.ev[a], self.ev[b])]
 
 
-def timed_step(path, q, k, v, out, p, kf, tm: StageTimer | None, balanced=True):
+def timed_step(path, q, k, v, out, p, kf, tm: StageTimer | None, balanced=True,
+               runtime=True):
     if tm: tm.mark("s0")
     path.order()
     if tm: tm.mark("s1")
@@ -141,20 +142,20 @@ def timed_step(path, q, k, v, out, p, kf, tm: StageTimer | None, balanced=True):
     if tm: tm.mark("s3")
     path.schedule()
     if tm: tm.mark("s4")
-    path.attend(balanced=balanced)
+    path.attend(balanced=balanced, runtime=runtime)
     if tm: tm.mark("s5")
     path.to_tokens(out)
     if tm: tm.mark("s6")
 
 
-def run_steps(path, q, k, v, out, p, kf, steps, warmup, balanced=True):
+def run_steps(path, q, k, v, out, p, kf, steps, warmup, balanced=True, runtime=True):
     for _ in range(warmup):
-        timed_step(path, q, k, v, out, p, kf, None, balanced)
+        timed_step(path, q, k, v, out, p, kf, None, balanced, runtime)
     torch.cuda.synchronize()
     tm = StageTimer()
     t0 = time.perf_counter()
     for _ in range(steps):
-        timed_step(path, q, k, v, out, p, kf, tm, balanced)
+        timed_step(path, q, k, v, out, p, kf, tm, balanced, runtime)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     names = ["hilbert", "permute_in", "route", "schedule", "attention", "permute_out"]
@@ -288,12 +289,19 @@ def main():
         o2 = torch.empty_like(q)
         _, _, st_grid = run_steps(path, q, k, v, o2, w.p, w.k, max(2, args.dense_steps), 1,
                                   balanced=False)
+        log("static LPT control")
+        _, _, st_static = run_steps(path, q, k, v, o2, w.p, w.k, max(2, args.dense_steps), 1,
+                                    runtime=False)
+        imb_static = cu_imbalance(path.timing.cpu().numpy())
         log("dense p=1 control")
         _, _, st_dense = run_steps(path, q, k, v, o2, 1.0, 0, args.dense_steps, 1)
         dense_flops = kept_flops(path)
         res["controls"] = {
             "head_major_attention_ms": round(st_grid["attention"], 4),
             "lpt_speedup_over_head_major": round(st_grid["attention"] / attn_ms, 4),
+            "static_lpt_attention_ms": round(st_static["attention"], 4),
+            "static_lpt_cu_max_over_mean": round(imb_static["max_over_mean"], 4),
+            "runtime_speedup_over_static_lpt": round(st_static["attention"] / attn_ms, 4),
             "dense_attention_ms": round(st_dense["attention"], 4),
             "dense_tflops": round(dense_flops / (st_dense["attention"] * 1e-3) / 1e12, 2),
             "speedup_vs_dense_attention": round(st_dense["attention"] / attn_ms, 4),

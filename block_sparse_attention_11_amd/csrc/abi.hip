@@ -121,7 +121,8 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
                        float scale,
                        const int32_t* kv_count, const int32_t* kv_index,
                        const int32_t* worker_offsets, const int32_t* worker_tiles,
-                       int n_workers, uint64_t* timing, hipStream_t stream) {
+                       int n_workers, uint64_t* timing, int32_t* claims,
+                       hipStream_t stream) {
   if (!q || !k || !v || !o || !kv_count || !kv_index) return FVATTN_EINVAL;
   if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
   if (isnan(scale) || isinf(scale)) return FVATTN_EINVAL;
@@ -137,11 +138,11 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   if (!fvattn::attn_has_mfma_instance(bf16, d, block) && (d > 128 || block > 256))
     return FVATTN_EUNSUPPORTED;
   // the tiled-V kernel addresses each tensor with one 32-bit buffer offset;
-  // tiles exist only for blocks of a multiple of 8 rows (fvattn_pack_v)
+  // tiles exist only for blocks of a multiple of 16 rows (fvattn_pack_v)
   if (v_layout == FVATTN_V_TILES &&
       ((long long)heads * nb * block * d * 2 > 0x7fffffffLL || block % 16 != 0))
     return FVATTN_EUNSUPPORTED;
-  if (timing && !worker_offsets) return FVATTN_EINVAL;
+  if ((timing || claims) && !worker_offsets) return FVATTN_EINVAL;
   fvattn::AttnArgs a;
   a.q = q;
   a.k = k;
@@ -160,6 +161,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   a.worker_tiles = worker_tiles;
   a.n_workers = worker_offsets ? n_workers : 0;
   a.timing = timing;
+  a.claims = claims;
   a.v_tiles = v_layout == FVATTN_V_TILES;
   a.group = group;
   a.tiles_per_head = (int)((nb + group - 1) / group);

@@ -809,16 +809,21 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   uint64_t t0 = 0;
   if (PERSIST && a.timing && tid == 0) stamp_start(t0);
   int beg = blockIdx.x, end = blockIdx.x + 1;
+  // run-time balancing: the tiles come from claims instead of this
+  // workgroup's list alone (see claim below); `end` is then only a sentinel
+  const bool dyn = PERSIST && a.claims != nullptr;
   if (PERSIST) {
     beg = ld_uniform(a.worker_offsets + blockIdx.x);
     end = ld_uniform(a.worker_offsets + blockIdx.x + 1);
   }
+  if (dyn) end = 0x7fffffff;
 
-  // walk state (wave-uniform): position in the worker list, the pair, the
-  // two list cursors and the current union block
+  // walk state (wave-uniform): position in the worker list (a position in
+  // worker_tiles), the pair, the two list cursors, the current union block,
+  // and the tile's ordinal in this workgroup's sequence
   struct Walk {
-    int it, h, i0, ca, cb, pa, pb, u;
-    bool ina, inb;
+    int it, h, i0, ca, cb, pa, pb, u, ord;
+    bool ina, inb, first;
   };
   auto list_at = [&](int h, int i, int p) {
     return min(max(ld_uniform(a.kv_index + ((size_t)h * nb + i) * nb + p), 0), nb - 1);
@@ -841,8 +846,114 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
           *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * r4 + 4 * g) = u32x2{0u, 0u};
     }
   };
-  // open the tile at list position it, or the next non-empty one
+  // Run-time balancing.  Counter claims[w] counts the tiles of worker w's
+  // LPT list handed out so far.  A workgroup takes the next tile of its own
+  // list while there is one, then the next tile of the list with the most
+  // tiles left; every hand-out is one atomic add, so each tile runs exactly
+  // once whichever workgroup runs it.  Wave 0 makes the claims, two tiles
+  // ahead, and posts the list positions in an LDS ring; the other waves read
+  // a slot at least one barrier after it was written.  Pairs with no kept
+  // block are written as zeros by wave 0 while claiming.
+  __shared__ int mbox[4];
+  bool own_done = false;
+  const int end_own = PERSIST ? ld_uniform(a.worker_offsets + blockIdx.x + 1) : end;
+  auto claim = [&]() -> int {
+    const int W = a.n_workers;
+    const int own = blockIdx.x;
+    while (true) {
+      int pos = -1;
+      if (!own_done) {
+        int j = 0;
+        if (lane == 0) j = atomicAdd(a.claims + own, 1);
+        j = __builtin_amdgcn_readfirstlane(j);
+        if (j < end_own - beg) pos = beg + j;
+        else own_done = true;
+      }
+      if (pos < 0) {
+        // the list with the most unclaimed tiles (ties: lowest index)
+        int best_rem = 0, best_v = -1;
+        for (int base = 0; base < W; base += 64) {
+          const int v = base + lane;
+          int rem = 0;
+          if (v < W && v != own) {
+            const int lo = a.worker_offsets[v], hi = a.worker_offsets[v + 1];
+            rem = hi - lo - __hip_atomic_load(a.claims + v, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+          }
+          int bv = rem > 0 ? v : -1;
+#pragma unroll
+          for (int m = 32; m >= 1; m >>= 1) {
+            const int orem = __shfl_xor(rem, m, 64);
+            const int ov = __shfl_xor(bv, m, 64);
+            if (orem > rem || (orem == rem && ov >= 0 && (bv < 0 || ov < bv))) {
+              rem = orem;
+              bv = ov;
+            }
+          }
+          if (rem > best_rem) {
+            best_rem = rem;
+            best_v = bv;
+          }
+        }
+        best_v = __builtin_amdgcn_readfirstlane(best_v);
+        if (best_v < 0) return -1;                 // every list is exhausted
+        int j = 0;
+        if (lane == 0) j = atomicAdd(a.claims + best_v, 1);
+        j = __builtin_amdgcn_readfirstlane(j);
+        const int lo = ld_uniform(a.worker_offsets + best_v);
+        const int hi = ld_uniform(a.worker_offsets + best_v + 1);
+        if (j >= hi - lo) continue;                // lost the race for it
+        pos = lo + j;
+      }
+      const int tile = ld_uniform(a.worker_tiles + pos);
+      const int h = tile / tph;
+      const int i0 = (tile - h * tph) * 2;
+      const int ca = ld_uniform(a.kv_count + (size_t)h * nb + i0);
+      const int cb = i0 + 1 < nb ? ld_uniform(a.kv_count + (size_t)h * nb + i0 + 1) : 0;
+      if (ca > 0 || cb > 0) return pos;
+      // nothing kept: zero both q-blocks' rows here
+      for (int r = lane; r < 2 * BLK; r += 64) {
+        const int qr = i0 * BLK + r;
+        if (qr < n) {
+          u32x4* orow = reinterpret_cast<u32x4*>(O + ((size_t)h * n + qr) * D);
+#pragma unroll
+          for (int c = 0; c < D / 8; ++c) orow[c] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  };
+  if (dyn) {
+    if (wave == 0) {
+      const int c0 = claim();
+      const int c1 = claim();
+      if (lane == 0) {
+        mbox[0] = c0;
+        mbox[1] = c1;
+      }
+    }
+    lds_barrier();
+  }
+  int ntile = 0;                                // tiles opened so far
+  // open the tile at list position it (static lists), or the next claimed
+  // one; skips tiles with nothing kept
   auto open_tile = [&](Walk& w, int it) {
+    if (dyn) {
+      const int pos = __builtin_amdgcn_readfirstlane(mbox[ntile & 3]);
+      w.ord = ntile++;
+      w.first = true;
+      if (pos < 0) {
+        w.it = end;
+        return;
+      }
+      const int tile = ld_uniform(a.worker_tiles + pos);
+      const int h = tile / tph;
+      const int i0 = (tile - h * tph) * 2;
+      w.it = pos; w.h = h; w.i0 = i0; w.pa = 0; w.pb = 0;
+      w.ca = min(ld_uniform(a.kv_count + (size_t)h * nb + i0), nb);
+      w.cb = i0 + 1 < nb ? min(ld_uniform(a.kv_count + (size_t)h * nb + i0 + 1), nb) : 0;
+      set_block(w);
+      return;
+    }
     while (it < end) {
       const int tile = PERSIST ? ld_uniform(a.worker_tiles + it) : it;
       const int h = tile / tph;
@@ -851,6 +962,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
       const int cb = i0 + 1 < nb ? min(ld_uniform(a.kv_count + (size_t)h * nb + i0 + 1), nb) : 0;
       if (ca > 0 || cb > 0) {
         w.it = it; w.h = h; w.i0 = i0; w.ca = ca; w.cb = cb; w.pa = 0; w.pb = 0;
+        w.ord = 0; w.first = true;
         set_block(w);
         return;
       }
@@ -862,6 +974,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   auto advance = [&](Walk w) {
     w.pa += w.ina;
     w.pb += w.inb;
+    w.first = false;
     if (w.pa >= w.ca && w.pb >= w.cb) open_tile(w, w.it + 1);
     else set_block(w);
     return w;
@@ -914,6 +1027,11 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
     wait_vmcnt<0>();
     lds_barrier();
     if (nxt.it < end) dma(kn, vn, nxt.h, nxt.u);
+    if (dyn && cur.first && wave == 0) {
+      // the tile two ahead of this one; its slot was last read two tiles ago
+      const int c = claim();
+      if (lane == 0) mbox[(cur.ord + 2) & 3] = c;
+    }
     const bool mine = grp == 0 ? cur.ina : cur.inb;
     if (mine) {
       // the block in halves of HK keys: an online-softmax step per half keeps
@@ -1019,8 +1137,17 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
 #endif
 }
 
+__global__ void claims_reset_kernel(int32_t* c, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) c[i] = 0;
+}
+
 template <int D, int BLK>
 hipError_t launch_mfma_pair(const AttnArgs& a, hipStream_t s) {
+  if (a.worker_offsets && a.claims) {
+    hipLaunchKernelGGL(claims_reset_kernel, dim3((a.n_workers + 255) / 256), dim3(256), 0, s,
+                       a.claims, a.n_workers);
+  }
   if (a.worker_offsets) {
     hipLaunchKernelGGL((attn_mfma_pair_kernel<D, BLK, true>), dim3(a.n_workers),
                        dim3(4 * BLK), 0, s, a);

@@ -73,6 +73,7 @@ struct AttnArgs {
   const int32_t* worker_tiles;
   int n_workers;
   uint64_t* timing;               // null or [n_workers][4]
+  int32_t* claims;                // null or [n_workers] claim counters (run-time balancing)
   bool v_tiles;                   // V as [heads][nb][d][block] transposed tiles
   int group;                      // q-blocks per tile (1 or 2)
   int tiles_per_head;             // ceil(nb / group)

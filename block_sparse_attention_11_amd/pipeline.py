@@ -71,6 +71,8 @@ class FVAttnPath:
         self.sched_ws = torch.empty(_lib.schedule_workspace_size(H, nb, W),
                                     dtype=torch.uint8, device=dev)
         self.timing = torch.zeros((W, 4), dtype=torch.int64, device=dev)
+        # claim counters for run-time balancing of the persistent launch
+        self.claims = torch.zeros(W, dtype=torch.int32, device=dev)
         self.ordered = False
 
     # -- steps -------------------------------------------------------------
@@ -95,13 +97,15 @@ class FVAttnPath:
                       self.worker_tiles, self.worker_load, self.sched_ws,
                       tile_order=self.tile_order, group=self.group)
 
-    def attend(self, balanced: bool = True, timing: bool = True):
+    def attend(self, balanced: bool = True, timing: bool = True, runtime: bool = True):
+        """balanced: persistent launch over the LPT lists (else the head-major
+        grid control); runtime: with run-time claims on top of the lists."""
         if balanced:
             _lib.sparse_attn(self.qh, self.kh, self.vh, self.oh, self.block,
                              self.kv_count, self.kv_index, self.worker_offsets,
                              self.worker_tiles, self.n_workers,
                              self.timing if timing else None, v_tiles=self.v_tiles,
-                             group=self.group)
+                             group=self.group, claims=self.claims if runtime else None)
         else:
             _lib.sparse_attn(self.qh, self.kh, self.vh, self.oh, self.block,
                              self.kv_count, self.kv_index, v_tiles=self.v_tiles,
@@ -110,7 +114,8 @@ class FVAttnPath:
     def to_tokens(self, out):
         _lib.permute_rows(self.oh, out, self.inv_perm)
 
-    def run(self, q, k, v, p: float, k_floor: int, out=None, balanced: bool = True):
+    def run(self, q, k, v, p: float, k_floor: int, out=None, balanced: bool = True,
+            runtime: bool = True):
         """One pass of the whole path; returns O in token order."""
         if out is None:
             out = torch.empty_like(q)
@@ -119,6 +124,6 @@ class FVAttnPath:
         self.to_hilbert(q, k, v)
         self.route(p, k_floor)
         self.schedule()
-        self.attend(balanced)
+        self.attend(balanced, runtime=runtime)
         self.to_tokens(out)
         return out

@@ -216,8 +216,21 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
  * timing (nullable, device uint64 [n_workers][4], persistent launch only):
  *   {start, end} of each workgroup on the 100 MHz constant clock
  *   (s_memrealtime), the raw HW_ID register and the XCC_ID register.
+ * claims (nullable, device int32 [n_workers], persistent launch only):
+ *   run-time balancing on top of the LPT lists, the single-GPU image of the
+ *   pages' runtime load balancing (aixai.ru FVAttn post, "Runtime Load
+ *   Balancing (RLB)"): the LPT plan predicts loads, the hardware's per-CU
+ *   speed differs, so a workgroup that finishes its own list early takes the
+ *   next unstarted tile of the list with the most tiles left.  claims[w]
+ *   counts the tiles of list w handed out; the call resets the array (with a
+ *   kernel on `stream`) and the attention kernel updates it with atomics, so
+ *   the caller only owns the memory, and calls that share it must not
+ *   overlap.  Every tile still runs exactly once, in one workgroup, so the
+ *   output is the same bits as without claims.  Honoured by the q-block-pair
+ *   kernel (group 2, FVATTN_V_TILES, an MFMA shape); the other kernels run
+ *   their lists as given.
  * Kernels: bf16 with (d, block) in {(64, 64), (128, 128), (64, 128),
- * (128, 64)} runs on an MFMA kernel (the LDS-DMA one for FVATTN_V_TILES);
+ * (128, 64)} runs on an MFMA kernel (the LDS-DMA ones for FVATTN_V_TILES);
  * every other (dtype, d <= 128, block <= 256) combination runs on a plain
  * fp32 VALU kernel.
  */
@@ -227,7 +240,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o,
                        const int32_t* kv_count,
                        const int32_t* kv_index, const int32_t* worker_offsets,
                        const int32_t* worker_tiles, int n_workers,
-                       uint64_t* timing, hipStream_t stream);
+                       uint64_t* timing, int32_t* claims, hipStream_t stream);
 
 /*
  * Persistent workers for fvattn_sparse_attn on the current device: the

@@ -338,6 +338,63 @@ def test_attention_handmade_lists(dtype, d, block, v_tiles, group):
         assert np.abs(got[h, r0:r1] - exp[h, r0:r1]).max() <= tol["max_abs"]
 
 
+@pytest.mark.parametrize("layout", ["one_list", "round_robin", "reversed", "more_workers"])
+def test_runtime_claims(layout):
+    """Run-time balancing: with claim counters the workgroups take tiles from
+    other workers' lists; every tile still runs once, in one workgroup, so the
+    output equals the static-list run bit for bit.  Includes a pair with
+    nothing kept (zeroed by the claiming workgroup)."""
+    w = workload("mid_bf16")
+    say(f"runtime claims {layout}")
+    q, k, v, _ = synth.make_inputs(w, "cpu")
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, device=DEV)
+    assert path.group == 2 and path.v_tiles
+    path.order()
+    path.to_hilbert(q.to(DEV), k.to(DEV), v.to(DEV))
+    path.route(w.p, w.k)
+    cnt = path.kv_count.clone()
+    cnt[1, 2:4] = 0                                 # head 1, pair 1: nothing kept
+    tph = (path.nb + 1) // 2
+    T = w.heads * tph
+    tiles = list(range(T))
+    if layout == "one_list":
+        W, lists = 4, [tiles, [], [], []]
+    elif layout == "round_robin":
+        W, lists = 3, [tiles[i::3] for i in range(3)]
+    elif layout == "reversed":
+        W, lists = 2, [tiles[::-1][:2], tiles[::-1][2:]]
+    else:
+        W, lists = T + 5, [[t] for t in tiles] + [[] for _ in range(5)]
+    off = np.zeros(W + 1, dtype=np.int32)
+    off[1:] = np.cumsum([len(x) for x in lists])
+    wt = np.array([t for x in lists for t in x], dtype=np.int32)
+    off_t = torch.from_numpy(off).to(DEV)
+    wt_t = torch.from_numpy(wt).to(DEV)
+    outs = []
+    claims = torch.full((W,), -7, dtype=torch.int32, device=DEV)
+    for use in (False, True):
+        path.oh.fill_(float("nan"))
+        _lib.sparse_attn(path.qh, path.kh, path.vh, path.oh, w.block, cnt, path.kv_index,
+                         off_t, wt_t, W, v_tiles=True, group=2,
+                         claims=claims if use else None)
+        torch.cuda.synchronize()
+        outs.append(path.oh.clone())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    got = to_np(outs[1])
+    assert (got[1, 2 * w.block:4 * w.block] == 0).all()
+    c = claims.cpu().numpy()
+    assert (c >= np.diff(off)).all()                 # every list was drained
+    perm = path.perm.cpu().numpy()
+    qh, kh, vh = (ort.permute_rows(to_np(x).astype(np.float64), perm) for x in (q, k, v))
+    cn = cnt.cpu().numpy()
+    kept_tiles = [(h, i) for h in range(w.heads) for i in range(path.nb) if cn[h, i] > 0]
+    ref = oat.block_sparse_attention(qh, kh, vh, w.block, cn, path.kv_index.cpu().numpy(),
+                                     tiles=kept_tiles)
+    keep = ~np.isnan(ref)
+    err = attn_errors(got[keep], ref[keep])
+    assert err["max_abs"] <= TOL["bf16"]["max_abs"] and err["rel_l2"] <= TOL["bf16"]["rel_l2"], err
+
+
 def test_rerun_is_bitwise_deterministic():
     w = workload("mid_bf16")
     say("determinism mid_bf16")
