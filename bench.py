@@ -218,6 +218,8 @@ def main():
     ap.add_argument("--workload", default="720p", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--workers", type=int, default=0, help="persistent workgroups (0 = CUs)")
     ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--group", type=int, default=0, choices=(0, 1, 2),
+                    help="q-blocks per tile (0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-controls", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -234,7 +236,7 @@ def main():
     q, k, v, meta = synth.make_inputs(w, "cuda")
     dt = q.dtype
     path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=dt,
-                      n_workers=args.workers or None, device="cuda")
+                      n_workers=args.workers or None, device="cuda", group=args.group or None)
     out = torch.empty_like(q)
 
     if args.copy_calibration:

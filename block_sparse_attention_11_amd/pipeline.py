@@ -29,7 +29,7 @@ def default_workers(device=None) -> int:
 
 class FVAttnPath:
     def __init__(self, heads: int, grid, d: int, block: int, dtype=torch.bfloat16,
-                 n_workers: int | None = None, device="cuda", tile_order: bool = True,
+                 n_workers: int | None = None, device="cuda", tile_order: bool = False,
                  v_tiles: bool | None = None, group: int | None = None):
         self.heads, self.grid, self.d, self.block = heads, tuple(grid), d, block
         T, Y, X = self.grid

@@ -75,11 +75,17 @@ WORKLOADS = {
                          note="40 heads, d=128, 41x45x80 tokens, block 128,"
                               " bf16; 4 steps with s_h redrawn per step"),
     # Supplementary, labelled: stronger Q/K coupling so routing is really sparse.
+    # Routed density per head at this shape (Hilbert blocks, p = 0.95, k = 8):
+    # s = 64 -> 0.89-0.92, s = 128 -> 0.54-0.88, s = 256 -> 0.02-0.58,
+    # s >= 512 -> near the Top-k floor (8/591), depending on r.
     "720p_sparse": Workload("720p_sparse", 40, 128, (21, 45, 80), 128, 0.95, 8,
-                            "bf16", s_range=(8.0, 256.0),
-                            flat_heads=tuple(range(32, 40)), flat_s=8.0,
+                            "bf16", s_range=(64.0, 1024.0),
+                            flat_heads=tuple(range(32, 40)), flat_s=64.0,
                             note="supplementary: 720p shape with s_h log-uniform"
-                                 " in [8, 256], heads 32-39 at s=8"),
+                                 " in [64, 1024], heads 32-39 at s=64 (dense, heavy)"),
+    # One rank's share of the 720p workload under 8-way head sharding.
+    "720p_rank": Workload("720p_rank", 5, 128, (21, 45, 80), 128, 0.95, 8, "bf16",
+                          note="720p, 5 of 40 heads (one of 8 ranks)"),
 }
 
 
