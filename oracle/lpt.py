@@ -24,6 +24,13 @@ One schedule is correct per input.
 Pins (tests/test_oracle_lpt.py): a hand-worked two-worker example,
 conservation, Graham's 4/3 - 1/(3W) bound against the brute-force optimum,
 the makespan <= mean + max-cost bound, W = 1 and W >= tiles.
+
+Two-level variant (lpt_schedule_grouped), a reading of the pages' balancing
+between ranks mapped onto the XCDs of one GPU: heads are first spread over
+X groups of workers (worker w is in group w % X) by the same LPT rule on
+head loads, then every tile goes, in the global LPT order, to the
+least-loaded worker of its head's group.  Pins: X = 1 gives lpt_schedule
+exactly; tiles stay in their head's group; conservation; a hand example.
 """
 from __future__ import annotations
 
@@ -75,3 +82,46 @@ def group_costs(kv_count, group: int) -> np.ndarray:
     for m in range(per):
         out[:, m] = kv[:, m * group:min(nb, (m + 1) * group)].sum(axis=1)
     return out.reshape(-1)
+
+
+def head_groups(head_loads: np.ndarray, groups: int) -> np.ndarray:
+    """LPT of heads over `groups` bins: heads in (load desc, head asc) order,
+    each to the least-loaded group (lowest index on ties).  Returns the group
+    of every head."""
+    loads = np.asarray(head_loads, dtype=np.int64).reshape(-1)
+    gl = np.zeros(groups, dtype=np.int64)
+    out = np.zeros(loads.shape[0], dtype=np.int32)
+    for h in lpt_order(loads):
+        x = int(np.argmin(gl))
+        out[h] = x
+        gl[x] += loads[h]
+    return out
+
+
+def lpt_schedule_grouped(costs_2d, n_workers: int, groups: int, tile_order: bool = False):
+    """Two-level LPT.  costs_2d [H, tiles per head]; worker w belongs to group
+    w % X with X = min(groups, n_workers).  Heads go to groups by LPT on their
+    summed tile costs; then each tile, in the global (cost desc, id asc)
+    order, goes to the least-loaded worker of its head's group (lowest index
+    on ties).  Returns (order, worker_offsets, worker_tiles, worker_load)
+    like lpt_schedule."""
+    c2 = np.asarray(costs_2d, dtype=np.int64)
+    H, tph = c2.shape
+    X = max(1, min(int(groups), n_workers))
+    hg = head_groups(c2.sum(axis=1), X)
+    costs = c2.reshape(-1)
+    order = lpt_order(costs)
+    loads = np.zeros(n_workers, dtype=np.int64)
+    members = [np.arange(x, n_workers, X) for x in range(X)]
+    lists = [[] for _ in range(n_workers)]
+    for t in order:
+        ws = members[hg[t // tph]]
+        w = int(ws[np.argmin(loads[ws])])        # first minimum = lowest index
+        lists[w].append(int(t))
+        loads[w] += costs[t]
+    if tile_order:
+        lists = [sorted(x) for x in lists]
+    offsets = np.zeros(n_workers + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum([len(x) for x in lists])
+    tiles = np.array([t for x in lists for t in x], dtype=np.int32)
+    return order, offsets, tiles, loads

@@ -97,3 +97,60 @@ def test_tile_order_keeps_the_assignment(seed):
     for w in range(W):
         a, b = t1[off1[w]:off1[w + 1]], t2[off2[w]:off2[w + 1]]
         assert sorted(a.tolist()) == b.tolist()
+
+
+# --- two-level (grouped) LPT ------------------------------------------------
+@pytest.mark.parametrize("seed", range(4))
+def test_grouped_with_one_group_is_plain_lpt(seed):
+    rng = np.random.default_rng(300 + seed)
+    H, tph = int(rng.integers(1, 6)), int(rng.integers(1, 40))
+    costs = rng.integers(0, 50, size=(H, tph))
+    W = int(rng.integers(1, 20))
+    for tile_order in (False, True):
+        a = lpt.lpt_schedule(costs.reshape(-1), W, tile_order=tile_order)
+        b = lpt.lpt_schedule_grouped(costs, W, 1, tile_order=tile_order)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+def test_head_groups_hand_example():
+    # loads 9, 7, 6, 5, 2 over 2 groups: 9->0, 7->1, 6->1 (7 < 9), 5->0 (9 < 13),
+    # 2->1 (13 < 14)
+    assert lpt.head_groups(np.array([6, 9, 2, 7, 5]), 2).tolist() == [1, 0, 1, 1, 0]
+
+
+def test_grouped_hand_example():
+    # 2 heads x 3 tiles, 4 workers in 2 groups (workers 0, 2 | 1, 3)
+    costs = np.array([[5, 1, 4],      # head 0, load 10 -> group 0
+                      [3, 3, 2]])     # head 1, load 8  -> group 1
+    order, off, tiles, loads = lpt.lpt_schedule_grouped(costs, 4, 2)
+    # global order: 0(5) 2(4) 3(3) 4(3) 5(2) 1(1)
+    assert order.tolist() == [0, 2, 3, 4, 5, 1]
+    lists = [tiles[off[w]:off[w + 1]].tolist() for w in range(4)]
+    assert lists == [[0], [3, 5], [2, 1], [4]]
+    assert loads.tolist() == [5, 5, 5, 3]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_grouped_tiles_stay_in_their_group(seed):
+    rng = np.random.default_rng(400 + seed)
+    H, tph = int(rng.integers(1, 12)), int(rng.integers(1, 30))
+    costs = rng.integers(0, 60, size=(H, tph))
+    W = int(rng.integers(1, 40))
+    X = int(rng.integers(1, 10))
+    order, off, tiles, loads = lpt.lpt_schedule_grouped(costs, W, X)
+    Xe = min(X, W)
+    hg = lpt.head_groups(costs.sum(1), Xe)
+    assert sorted(tiles.tolist()) == list(range(H * tph))
+    assert loads.sum() == costs.sum()
+    for w in range(W):
+        mine = tiles[off[w]:off[w + 1]]
+        assert loads[w] == costs.reshape(-1)[mine].sum()
+        assert all(hg[t // tph] == w % Xe for t in mine)
+    # inside a group the greedy keeps the LPT bound: makespan <= mean + max
+    for x in range(Xe):
+        ws = np.arange(x, W, Xe)
+        tl = np.concatenate([tiles[off[w]:off[w + 1]] for w in ws])
+        if tl.size:
+            c = costs.reshape(-1)[tl]
+            assert loads[ws].max() <= c.sum() / ws.size + c.max() + 1e-9
