@@ -22,6 +22,11 @@ HEADER = os.path.join(ROOT, "include", "fvattn.h")
 OK, EINVAL, EUNSUPPORTED, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 SCHED_TILE_ORDER = 1
+
+
+def SCHED_GROUPS(x: int) -> int:
+    """fvattn_schedule flag for the two-level LPT over x worker groups."""
+    return int(x) << 8
 V_ROWS, V_TILES = 0, 1
 
 _c_void_p = ctypes.c_void_p
@@ -187,8 +192,10 @@ def schedule_workspace_size(heads: int, n_qblocks: int, n_workers: int) -> int:
 
 
 def schedule(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
-             worker_load, workspace, tile_order: bool = False, group: int = 1):
-    """LPT lists over tiles of `group` q-blocks (tiles = H * ceil(nB / group))."""
+             worker_load, workspace, tile_order: bool = False, group: int = 1,
+             worker_groups: int = 1):
+    """LPT lists over tiles of `group` q-blocks (tiles = H * ceil(nB / group));
+    worker_groups > 1 selects the two-level LPT (heads to groups w % x)."""
     _dev(kv_count, lpt_order, worker_offsets, worker_tiles, worker_load, workspace)
     _need(kv_count.dim() == 2 and kv_count.dtype == torch.int32, "kv_count i32[H, nB]")
     H, nb = kv_count.shape
@@ -200,7 +207,8 @@ def schedule(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("fvattn_schedule", load_library().fvattn_schedule(
         _ptr(kv_count), H, nb, int(group), int(n_workers),
-        SCHED_TILE_ORDER if tile_order else 0,
+        (SCHED_TILE_ORDER if tile_order else 0)
+        | (SCHED_GROUPS(worker_groups) if worker_groups > 1 else 0),
         _ptr(lpt_order), _ptr(worker_offsets),
         _ptr(worker_tiles), _ptr(worker_load), _ptr(workspace), ws_bytes,
         _stream(kv_count)))

@@ -107,12 +107,18 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group
   if (heads < 1 || n_qblocks < 1 || n_workers < 1) return FVATTN_EINVAL;
   if (group != 1 && group != 2) return FVATTN_EINVAL;
   if (!fits_int32((long long)heads * n_qblocks)) return FVATTN_EINVAL;
-  if (flags & ~FVATTN_SCHED_TILE_ORDER) return FVATTN_EINVAL;
+  if (flags & ~(FVATTN_SCHED_TILE_ORDER | FVATTN_SCHED_GROUPS(0xFF))) return FVATTN_EINVAL;
   if (n_workers > fvattn::kMaxWorkers) return FVATTN_EUNSUPPORTED;
+  const int n_groups = (flags >> 8) & 0xFF;
+  if (n_groups > 1) {
+    if (n_groups > fvattn::schedule_max_groups() || n_groups > n_workers) return FVATTN_EINVAL;
+    if (heads > fvattn::schedule_max_group_heads()) return FVATTN_EUNSUPPORTED;
+  }
   const size_t need = fvattn::schedule_workspace_bytes(heads, n_qblocks, n_workers);
   if (!workspace || workspace_bytes < need) return FVATTN_EWORKSPACE;
   return launch_status(fvattn::launch_schedule(
-      kv_count, heads, n_qblocks, group, n_workers, (flags & FVATTN_SCHED_TILE_ORDER) != 0,
+      kv_count, heads, n_qblocks, group, n_workers, n_groups > 1 ? n_groups : 1,
+      (flags & FVATTN_SCHED_TILE_ORDER) != 0,
       lpt_order, worker_offsets, worker_tiles, worker_load, workspace, stream));
 }
 

@@ -55,9 +55,11 @@ constexpr int kMaxCost = 65535;
 size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers);
 // tiles = heads * ceil(n_qblocks / group); tile t = h * ceil(nq/group) + m
 hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group,
-                           int n_workers, bool tile_order, int32_t* lpt_order,
+                           int n_workers, int n_groups, bool tile_order, int32_t* lpt_order,
                            int32_t* worker_offsets, int32_t* worker_tiles,
                            int64_t* worker_load, void* ws, hipStream_t s);
+int schedule_max_groups();
+int schedule_max_group_heads();
 
 // ---- attn.hip --------------------------------------------------------------
 struct AttnArgs {

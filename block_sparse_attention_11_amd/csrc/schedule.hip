@@ -32,6 +32,18 @@
 //                      order: the same assignment and loads, executed
 //                      head-major inside every worker so that concurrently
 //                      running workgroups share K/V blocks in L2).
+//
+// Two-level variant (X > 1 worker groups; worker w is in group w % X, which
+// is the XCD a persistent workgroup w runs on when X is the XCD count): the
+// pages balance heavy heads between ranks; here heads are spread over the
+// groups by the same LPT rule on head loads, and every tile then goes, in the
+// global LPT order, to the least-loaded worker of its head's group.  Tiles of
+// one head then share one XCD's L2.
+//   head_group_kernel      head loads, heads sorted by (load desc, id asc)
+//                          in LDS, greedy over the groups in one wavefront
+//   group_partition_kernel stable split of the LPT order by group
+//   lpt_assign_kernel      one workgroup per group on its slice
+//   worker_offsets_kernel  list offsets from the per-worker counts
 #include "device_util.h"
 #include "internal.h"
 
@@ -51,20 +63,24 @@ struct SchedWs {
   int32_t* slot;    // its position in that worker's list
   int32_t* owner_by_tile;  // worker of tile t
   int32_t* group_cost;     // per-tile cost when a tile spans several q-blocks
+  int32_t* head_group;     // two-level: group of every head
+  int32_t* gseq;           // two-level: LPT order split by group
+  int32_t* wcount;         // two-level: tiles per worker [kMaxWorkers]
+  int32_t* goff;           // two-level: start of each group's slice [kMaxGroups + 1]
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+constexpr int kMaxGroups = 64;
+constexpr size_t kSmallSlab = (kMaxWorkers + kMaxGroups + 1) * sizeof(int32_t);
+
 SchedWs carve(void* ws, int tiles) {
   const size_t one = align_up(sizeof(int32_t) * (size_t)tiles, 256);
   char* b = static_cast<char*>(ws);
-  return SchedWs{reinterpret_cast<int32_t*>(b), reinterpret_cast<int32_t*>(b + one),
-                 reinterpret_cast<int32_t*>(b + 2 * one),
-                 reinterpret_cast<int32_t*>(b + 3 * one),
-                 reinterpret_cast<int32_t*>(b + 4 * one),
-                 reinterpret_cast<int32_t*>(b + 5 * one),
-                 reinterpret_cast<int32_t*>(b + 6 * one),
-                 reinterpret_cast<int32_t*>(b + 7 * one)};
+  auto at = [&](size_t i) { return reinterpret_cast<int32_t*>(b + i * one); };
+  int32_t* small = at(10);
+  return SchedWs{at(0), at(1), at(2), at(3), at(4), at(5), at(6), at(7), at(8), at(9),
+                 small, small + kMaxWorkers};
 }
 
 __device__ inline int clamp_cost(int c) { return min(max(c, 0), kMaxCost); }
@@ -159,10 +175,24 @@ constexpr int kAssignThreads = 1024;
 constexpr int kMaxWorkersPow2 = 2048;
 constexpr int kWorkerBits = 11;
 
+// Single level (goff == null): block 0 assigns seq[0 .. tiles) over all
+// n_workers workers and also writes the list offsets.  Two-level: block x
+// assigns the slice seq[goff[x] .. goff[x+1]) over workers x, x+X, x+2X, ...
+// and leaves the offsets to worker_offsets_kernel.  owner/slot are indexed by
+// the position in seq.
 __global__ __launch_bounds__(kAssignThreads) void lpt_assign_kernel(
-    const int32_t* __restrict__ cost, const int32_t* __restrict__ lpt_order,
-    int tiles, int n_workers, SchedWs ws, int32_t* __restrict__ worker_offsets,
-    int64_t* __restrict__ worker_load) {
+    const int32_t* __restrict__ cost, const int32_t* __restrict__ seq_all,
+    int tiles_all, int n_workers_all, const int32_t* __restrict__ goff, int n_groups,
+    SchedWs ws, int32_t* __restrict__ worker_offsets, int64_t* __restrict__ worker_load) {
+  const int grp = blockIdx.x;
+  const int base_pos = goff ? goff[grp] : 0;
+  const int tiles = goff ? goff[grp + 1] - base_pos : tiles_all;
+  const int32_t* lpt_order = seq_all + base_pos;
+  const int n_workers = goff ? (n_workers_all - grp + n_groups - 1) / n_groups : n_workers_all;
+  // local worker j is global worker wg(j)
+  auto wg = [&](int j) { return goff ? grp + j * n_groups : j; };
+  int32_t* owner = ws.owner + base_pos;
+  int32_t* slotp = ws.slot + base_pos;
   __shared__ uint64_t key[kMaxWorkersPow2];
   __shared__ uint64_t tmp[kMaxWorkersPow2];
   __shared__ int32_t cnt[kMaxWorkersPow2];
@@ -218,8 +248,8 @@ __global__ __launch_bounds__(kAssignThreads) void lpt_assign_kernel(
       const int w0 = (int)(key[0] & ((1u << kWorkerBits) - 1));
       const int base = cnt[w0];
       for (int t = k + tid; t < tiles; t += kAssignThreads) {
-        ws.owner[t] = w0;
-        ws.slot[t] = base + (t - k);
+        owner[t] = wg(w0);
+        slotp[t] = base + (t - k);
       }
       __syncthreads();
       if (tid == 0) cnt[w0] = base + (tiles - k);
@@ -249,8 +279,8 @@ __global__ __launch_bounds__(kAssignThreads) void lpt_assign_kernel(
       const uint64_t kx = key[x];
       const int w = (int)(kx & ((1u << kWorkerBits) - 1));
       const uint32_t c = (uint32_t)clamp_cost(cost[lpt_order[k + x]]);
-      ws.owner[k + x] = w;
-      ws.slot[k + x] = cnt[w];
+      owner[k + x] = wg(w);
+      slotp[k + x] = cnt[w];
       cnt[w] += 1;
       key[x] = kx + ((uint64_t)c << kWorkerBits);
     }
@@ -260,7 +290,16 @@ __global__ __launch_bounds__(kAssignThreads) void lpt_assign_kernel(
   }
 
   // owner by tile, list offsets and loads
-  for (int t = tid; t < tiles; t += kAssignThreads) ws.owner_by_tile[lpt_order[t]] = ws.owner[t];
+  for (int t = tid; t < tiles; t += kAssignThreads) ws.owner_by_tile[lpt_order[t]] = owner[t];
+  if (goff) {
+    for (int x = tid; x < n_workers; x += kAssignThreads) {
+      const uint64_t kx = key[x];
+      const int j = (int)(kx & ((1u << kWorkerBits) - 1));
+      worker_load[wg(j)] = (int64_t)(kx >> kWorkerBits);
+      ws.wcount[wg(j)] = cnt[j];
+    }
+    return;
+  }
   // exclusive scan of cnt over workers: contiguous chunk per thread
   const int per = (n_workers + kAssignThreads - 1) / kAssignThreads;
   const int lo = min(n_workers, tid * per), hi = min(n_workers, lo + per);
@@ -277,6 +316,124 @@ __global__ __launch_bounds__(kAssignThreads) void lpt_assign_kernel(
     const uint64_t kx = key[x];
     worker_load[kx & ((1u << kWorkerBits) - 1)] = (int64_t)(kx >> kWorkerBits);
   }
+}
+
+// Heads to groups: head loads (sums of their tile costs), heads sorted by
+// (load desc, id asc) with a bitonic sort in LDS, then the greedy in wave 0
+// (lane x holds group x's load; every head goes to the least-loaded group,
+// lowest index on ties).
+constexpr int kMaxGroupHeads = 4096;
+__global__ __launch_bounds__(1024) void head_group_kernel(
+    const int32_t* __restrict__ cost, int heads, int tph, int n_groups,
+    int32_t* __restrict__ head_group) {
+  __shared__ uint64_t key[kMaxGroupHeads];
+  __shared__ uint64_t load[kMaxGroupHeads];
+  const int tid = threadIdx.x;
+  int hp = 1;
+  while (hp < heads) hp <<= 1;
+  for (int h = tid; h < hp; h += 1024) {
+    uint64_t l = 0;
+    if (h < heads)
+      for (int m = 0; m < tph; ++m) l += (uint64_t)clamp_cost(cost[(size_t)h * tph + m]);
+    load[h] = l;
+    // ascending key = (load desc, head asc); loads stay below 2^47
+    key[h] = h < heads ? ((((1ull << 47) - 1 - l) << 12) | (uint64_t)h) : ~0ull;
+  }
+  __syncthreads();
+  for (int kk = 2; kk <= hp; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int x = tid; x < hp; x += 1024) {
+        const int y = x ^ jj;
+        if (y > x) {
+          const uint64_t a = key[x], b = key[y];
+          const bool up = (x & kk) == 0;
+          if (up ? (a > b) : (a < b)) {
+            key[x] = b;
+            key[y] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid < kWave) {
+    const int lane = tid;
+    uint64_t gl = lane < n_groups ? 0ull : ~0ull;
+    for (int r = 0; r < heads; ++r) {
+      const int h = (int)(key[r] & 4095u);
+      // least-loaded group, lowest index on ties
+      uint64_t best = gl;
+      int bx = lane;
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        const uint64_t ob = __shfl_xor(best, off, kWave);
+        const int ox = __shfl_xor(bx, off, kWave);
+        if (ob < best || (ob == best && ox < bx)) {
+          best = ob;
+          bx = ox;
+        }
+      }
+      if (lane == bx) {
+        gl += load[h];
+        head_group[h] = bx;
+      }
+    }
+  }
+}
+
+// Stable split of the LPT order by the group of each tile's head: seq lists
+// the positions of group 0 first, then group 1, ..., each in LPT order;
+// goff[x] is where group x starts.  Per-thread counts in LDS, scanned in
+// (group, thread) order.
+constexpr int kPartThreads = 256;
+__global__ __launch_bounds__(kPartThreads) void group_partition_kernel(
+    const int32_t* __restrict__ lpt_order, int tiles, int tph,
+    const int32_t* __restrict__ head_group, int n_groups, int32_t* __restrict__ seq,
+    int32_t* __restrict__ goff) {
+  __shared__ int32_t table[kMaxGroups * kPartThreads];   // [group][thread]
+  __shared__ int32_t s_scan[kPartThreads / kWave];
+  const int tid = threadIdx.x;
+  const int per = (tiles + kPartThreads - 1) / kPartThreads;
+  const int lo = min(tiles, tid * per), hi = min(tiles, lo + per);
+  for (int x = 0; x < kMaxGroups; ++x) table[x * kPartThreads + tid] = 0;
+  for (int k = lo; k < hi; ++k) table[head_group[lpt_order[k] / tph] * kPartThreads + tid] += 1;
+  __syncthreads();
+  // exclusive scan over (group, thread): thread u owns entries [u*64, u*64+64)
+  int run = 0;
+  int local[kMaxGroups];
+#pragma unroll
+  for (int e = 0; e < kMaxGroups; ++e) {
+    local[e] = run;
+    run += table[tid * kMaxGroups + e];
+  }
+  int total;
+  const int base = block_exclusive_scan<kPartThreads>(run, s_scan, total);
+#pragma unroll
+  for (int e = 0; e < kMaxGroups; ++e) table[tid * kMaxGroups + e] = base + local[e];
+  __syncthreads();
+  if (tid <= n_groups) goff[tid] = tid < n_groups ? table[tid * kPartThreads] : tiles;
+  for (int k = lo; k < hi; ++k) {
+    const int t = lpt_order[k];
+    seq[table[head_group[t / tph] * kPartThreads + tid]++] = t;
+  }
+}
+
+// worker_offsets from the per-worker counts of the two-level assignment
+__global__ __launch_bounds__(1024) void worker_offsets_kernel(
+    const int32_t* __restrict__ wcount, int n_workers, int32_t* __restrict__ worker_offsets) {
+  __shared__ int32_t s_scan[1024 / kWave];
+  const int tid = threadIdx.x;
+  const int per = (n_workers + 1023) / 1024;
+  const int lo = min(n_workers, tid * per), hi = min(n_workers, lo + per);
+  int run = 0;
+  for (int w = lo; w < hi; ++w) run += wcount[w];
+  int total;
+  int off = block_exclusive_scan<1024>(run, s_scan, total);
+  for (int w = lo; w < hi; ++w) {
+    worker_offsets[w] = off;
+    off += wcount[w];
+  }
+  if (tid == 0) worker_offsets[n_workers] = total;
 }
 
 // cost of tile t = (h, m) covering q-blocks [m*group, min(nq, (m+1)*group))
@@ -304,11 +461,14 @@ __global__ __launch_bounds__(256) void lpt_scatter_kernel(
 size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers) {
   (void)n_workers;
   const size_t tiles = (size_t)heads * n_qblocks;
-  return 8 * align_up(sizeof(int32_t) * tiles, 256);
+  return 10 * align_up(sizeof(int32_t) * tiles, 256) + align_up(kSmallSlab, 256);
 }
 
+int schedule_max_groups() { return kMaxGroups; }
+int schedule_max_group_heads() { return kMaxGroupHeads; }
+
 hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group,
-                           int n_workers, bool tile_order, int32_t* lpt_order,
+                           int n_workers, int n_groups, bool tile_order, int32_t* lpt_order,
                            int32_t* worker_offsets, int32_t* worker_tiles,
                            int64_t* worker_load, void* wsp, hipStream_t s) {
   const int per_head = (n_qblocks + group - 1) / group;
@@ -326,8 +486,23 @@ hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, in
                      tiles, ws, lpt_order, false);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lpt_assign_kernel, dim3(1), dim3(kAssignThreads), 0, s, cost,
-                     lpt_order, tiles, n_workers, ws, worker_offsets, worker_load);
+  const int X = min(n_groups, n_workers);
+  const int32_t* seq = lpt_order;
+  if (X > 1) {
+    hipLaunchKernelGGL(head_group_kernel, dim3(1), dim3(1024), 0, s, cost, heads, per_head, X,
+                       ws.head_group);
+    hipLaunchKernelGGL(group_partition_kernel, dim3(1), dim3(kPartThreads), 0, s, lpt_order,
+                       tiles, per_head, ws.head_group, X, ws.gseq, ws.goff);
+    hipLaunchKernelGGL(lpt_assign_kernel, dim3(X), dim3(kAssignThreads), 0, s, cost, ws.gseq,
+                       tiles, n_workers, ws.goff, X, ws, worker_offsets, worker_load);
+    hipLaunchKernelGGL(worker_offsets_kernel, dim3(1), dim3(1024), 0, s, ws.wcount, n_workers,
+                       worker_offsets);
+    seq = ws.gseq;
+  } else {
+    hipLaunchKernelGGL(lpt_assign_kernel, dim3(1), dim3(kAssignThreads), 0, s, cost,
+                       lpt_order, tiles, n_workers, (const int32_t*)nullptr, 1, ws,
+                       worker_offsets, worker_load);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (tile_order) {
@@ -335,7 +510,7 @@ hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, in
                        tiles, ws, worker_tiles, true);
   } else {
     hipLaunchKernelGGL(lpt_scatter_kernel, dim3((tiles + 255) / 256), dim3(256), 0, s,
-                       lpt_order, tiles, ws, worker_offsets, worker_tiles);
+                       seq, tiles, ws, worker_offsets, worker_tiles);
   }
   return hipGetLastError();
 }

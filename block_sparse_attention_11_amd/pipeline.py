@@ -18,6 +18,7 @@ import torch
 from . import _lib
 
 MAX_WORKERS = 2048          # fvattn_schedule's limit
+XCDS = 8                    # accelerator complex dies of an MI355X
 
 
 def default_workers(device=None) -> int:
@@ -30,13 +31,16 @@ def default_workers(device=None) -> int:
 class FVAttnPath:
     def __init__(self, heads: int, grid, d: int, block: int, dtype=torch.bfloat16,
                  n_workers: int | None = None, device="cuda", tile_order: bool = False,
-                 v_tiles: bool | None = None, group: int | None = None):
+                 v_tiles: bool | None = None, group: int | None = None,
+                 worker_groups: int | None = None):
         self.heads, self.grid, self.d, self.block = heads, tuple(grid), d, block
         T, Y, X = self.grid
         self.n = T * Y * X
         self.nb = (self.n + block - 1) // block
         self.dtype = dtype
         self.tile_order = tile_order
+        # two-level LPT over the XCDs: persistent workgroup w runs on XCD
+        # w % 8 of an MI355X, so 8 groups keep each head on one XCD
         self.device = torch.device(device)
         H, n, nb, dev = heads, self.n, self.nb, self.device
         i32 = dict(dtype=torch.int32, device=dev)
@@ -64,6 +68,9 @@ class FVAttnPath:
         self.route_ws = torch.empty(_lib.route_workspace_size(H, n, d, block),
                                     dtype=torch.uint8, device=dev)
         W = self.n_workers
+        if worker_groups is None:
+            worker_groups = XCDS if (W % XCDS == 0 and heads <= 4096) else 1
+        self.worker_groups = worker_groups
         self.lpt_order = torch.empty(self.tiles, **i32)
         self.worker_offsets = torch.empty(W + 1, **i32)
         self.worker_tiles = torch.empty(self.tiles, **i32)
@@ -95,7 +102,8 @@ class FVAttnPath:
     def schedule(self):
         _lib.schedule(self.kv_count, self.n_workers, self.lpt_order, self.worker_offsets,
                       self.worker_tiles, self.worker_load, self.sched_ws,
-                      tile_order=self.tile_order, group=self.group)
+                      tile_order=self.tile_order, group=self.group,
+                      worker_groups=self.worker_groups)
 
     def attend(self, balanced: bool = True, timing: bool = True, runtime: bool = True):
         """balanced: persistent launch over the LPT lists (else the head-major

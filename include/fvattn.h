@@ -55,6 +55,8 @@ extern "C" {
 
 /* fvattn_schedule flags. */
 #define FVATTN_SCHED_TILE_ORDER 1
+/* two-level LPT over x worker groups (2 <= x <= 64), see fvattn_schedule */
+#define FVATTN_SCHED_GROUPS(x) ((x) << 8)
 
 /* V layouts accepted by fvattn_sparse_attn. */
 #define FVATTN_V_ROWS 0    /* [heads][n][d], like Q and K                     */
@@ -176,6 +178,21 @@ int fvattn_route(const void* q, const void* k, int dtype, int heads, int n,
  *                            assignment and loads; a persistent kernel then
  *                            walks heads in step across workgroups, so K/V
  *                            blocks are shared in L2 while they run.
+ *   FVATTN_SCHED_GROUPS(x)   two-level LPT, the single-GPU image of the
+ *                            pages' balancing of heavy heads between ranks:
+ *                            worker w belongs to group w % x (x = the XCD
+ *                            count makes a group one XCD, since persistent
+ *                            workgroup w runs on XCD w % 8 on MI355X); head
+ *                            loads (sums of their tile costs) go to the
+ *                            groups by the same LPT rule (heads by (load
+ *                            desc, head asc), least-loaded group, lowest
+ *                            index on ties); then each tile, in lpt_order,
+ *                            goes to the least-loaded worker of its head's
+ *                            group (lowest index on ties).  Every head's
+ *                            K/V then stays in one XCD's L2.  x <= 64 and
+ *                            x <= n_workers (else FVATTN_EINVAL); heads <=
+ *                            4096 (else FVATTN_EUNSUPPORTED).  Combines
+ *                            with FVATTN_SCHED_TILE_ORDER.
  * Bit-exact: there is exactly one correct result per input and flag.
  * Limits: 1 <= n_workers <= 2048; tile costs are clamped to [0, 65535];
  * heads*n_qblocks < 2^31; group in {1, 2} (else FVATTN_EINVAL).

@@ -51,7 +51,9 @@ def test_workspace_sizes():
     rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert lib.fvattn_route_workspace_size(40, 75600, 128, 128) == 2 * rnd(pooled) + rnd(scores)
     assert lib.fvattn_route_workspace_size(0, 75600, 128, 128) == 0
-    assert lib.fvattn_schedule_workspace_size(40, 591, 256) == 8 * rnd(40 * 591 * 4)
+    # ten per-tile slabs plus counts/offsets for up to 2048 workers and 64 groups
+    assert lib.fvattn_schedule_workspace_size(40, 591, 256) == (
+        10 * rnd(40 * 591 * 4) + rnd((2048 + 65) * 4))
     assert lib.fvattn_schedule_workspace_size(40, 591, 0) == 0
 
 
@@ -87,6 +89,11 @@ def _validation_main():
         (lib.fvattn_schedule(P, 40, 591, 1, 0, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule(N, 40, 591, 1, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule(P, 40, 591, 1, 256, 1, P, P, P, P, P, 100, N), EWS),
+        # two-level LPT: at most 64 groups, no more groups than workers,
+        # at most 4096 heads
+        (lib.fvattn_schedule(P, 40, 591, 1, 256, 65 << 8, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule(P, 40, 591, 1, 4, 8 << 8, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule(P, 4097, 2, 1, 256, 8 << 8, P, P, P, P, P, 1 << 30, N), EUNS),
         # attention
         (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N), EINVAL),

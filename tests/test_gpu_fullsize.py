@@ -1,6 +1,6 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (default persistent worker count, V key-block tiles, q-block
-pairs, tile-ordered LPT lists).
+pairs, two-level LPT lists over the XCDs, run-time claims).
 
 At these sizes the oracle still runs every integer step in full (Hilbert
 order, routing of every row of every head, the LPT schedule), while the
@@ -89,7 +89,11 @@ def check_route(path, w, p, heads):
 
 def check_schedule(path):
     costs = olpt.group_costs(path.kv_count.cpu().numpy(), path.group)
-    ref = olpt.lpt_schedule(costs, path.n_workers, tile_order=path.tile_order)
+    if path.worker_groups > 1:
+        ref = olpt.lpt_schedule_grouped(costs.reshape(path.heads, -1), path.n_workers,
+                                        path.worker_groups, tile_order=path.tile_order)
+    else:
+        ref = olpt.lpt_schedule(costs, path.n_workers, tile_order=path.tile_order)
     got = (path.lpt_order, path.worker_offsets, path.worker_tiles, path.worker_load)
     for g, r, what in zip(got, ref, ("order", "offsets", "tiles", "loads")):
         assert np.array_equal(g.cpu().numpy(), r), what

@@ -181,7 +181,7 @@ def test_route_parity(name, p, kf):
 # ---------------------------------------------------------------------------
 # LPT schedule
 # ---------------------------------------------------------------------------
-def gpu_schedule(costs_2d, W, tile_order=False, group=1):
+def gpu_schedule(costs_2d, W, tile_order=False, group=1, worker_groups=1):
     H, nb = costs_2d.shape
     kvc = torch.from_numpy(costs_2d.astype(np.int32)).to(DEV)
     tiles = H * ((nb + group - 1) // group)
@@ -190,7 +190,8 @@ def gpu_schedule(costs_2d, W, tile_order=False, group=1):
     wt = torch.empty(tiles, dtype=torch.int32, device=DEV)
     wl = torch.empty(W, dtype=torch.int64, device=DEV)
     ws = torch.empty(_lib.schedule_workspace_size(H, nb, W), dtype=torch.uint8, device=DEV)
-    _lib.schedule(kvc, W, order, off, wt, wl, ws, tile_order=tile_order, group=group)
+    _lib.schedule(kvc, W, order, off, wt, wl, ws, tile_order=tile_order, group=group,
+                  worker_groups=worker_groups)
     torch.cuda.synchronize()
     return order.cpu().numpy(), off.cpu().numpy(), wt.cpu().numpy(), wl.cpu().numpy()
 
@@ -209,11 +210,15 @@ SCHED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("xg", [1, 8, 3])
 @pytest.mark.parametrize("group", [1, 2])
 @pytest.mark.parametrize("tile_order", [False, True])
 @pytest.mark.parametrize("name,costs,W", SCHED_CASES)
-def test_schedule_bit_exact(name, costs, W, tile_order, group):
-    say(f"schedule {name} W={W} tile_order={tile_order} group={group}")
+def test_schedule_bit_exact(name, costs, W, tile_order, group, xg):
+    X = min(xg, W)
+    if xg > 1 and X == 1:
+        pytest.skip("one worker: the two-level schedule is the plain one")
+    say(f"schedule {name} W={W} tile_order={tile_order} group={group} groups={X}")
     rng = np.random.default_rng(sum(map(ord, name)))
     if name == "random_ties":
         costs = rng.integers(1, 9, size=(8, 37))
@@ -223,8 +228,13 @@ def test_schedule_bit_exact(name, costs, W, tile_order, group):
         costs = rng.integers(8, 1155, size=(40, 1154))
     elif name == "big_costs":
         costs = rng.integers(0, 16384, size=(5, 333))
-    got = gpu_schedule(costs, W, tile_order, group)
-    ref = olpt.lpt_schedule(olpt.group_costs(costs, group), W, tile_order=tile_order)
+    got = gpu_schedule(costs, W, tile_order, group, X)
+    gc = olpt.group_costs(costs, group)
+    if X > 1:
+        ref = olpt.lpt_schedule_grouped(gc.reshape(costs.shape[0], -1), W, X,
+                                        tile_order=tile_order)
+    else:
+        ref = olpt.lpt_schedule(gc, W, tile_order=tile_order)
     for g, r, what in zip(got, ref, ("order", "offsets", "tiles", "loads")):
         assert np.array_equal(g, r), what
 
