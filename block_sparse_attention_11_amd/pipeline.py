@@ -40,7 +40,8 @@ class FVAttnPath:
         self.dtype = dtype
         self.tile_order = tile_order
         # two-level LPT over the XCDs: persistent workgroup w runs on XCD
-        # w % 8 of an MI355X, so 8 groups keep each head on one XCD
+        # w % 8 of an MI355X, so 8 groups keep each head on one XCD (used when
+        # there are at least two heads per group)
         self.device = torch.device(device)
         H, n, nb, dev = heads, self.n, self.nb, self.device
         i32 = dict(dtype=torch.int32, device=dev)
@@ -69,7 +70,8 @@ class FVAttnPath:
                                     dtype=torch.uint8, device=dev)
         W = self.n_workers
         if worker_groups is None:
-            worker_groups = XCDS if (W % XCDS == 0 and heads <= 4096) else 1
+            # at least two heads per group, or the head-level LPT cannot balance
+            worker_groups = XCDS if (W % XCDS == 0 and 2 * XCDS <= heads <= 4096) else 1
         self.worker_groups = worker_groups
         self.lpt_order = torch.empty(self.tiles, **i32)
         self.worker_offsets = torch.empty(W + 1, **i32)
