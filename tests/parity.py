@@ -7,8 +7,8 @@ A row of the GPU mask that differs from the oracle's is accepted only if the
 GPU's kept set S is itself a correct answer for the oracle's importances P
 within these windows:
   (a) count window: the accumulated mass at the cut is within MASS_WINDOW
-      (1e-4) of p, i.e. mass(S) >= p - 1e-4 and, when |S| > k, the mass
-      without S's weakest block is < p + 1e-4;
+      (1e-4) of p, i.e. mass(S) >= p - 1e-4 (at the Top-k floor as well) and,
+      when |S| > k, the mass without S's weakest block is < p + 1e-4;
   (b) order window (a reading beyond the stated count window, for rows whose
       importances are nearly uniform): every block in the symmetric
       difference has P within TIE_REL (1e-5) * max P of the cut value, so S is
@@ -64,12 +64,15 @@ def _accept(Prow, p, k, gs, os_):
     if pout.size and pin.min() < pout.max() - tie:
         return None
     mass = pin.sum()
-    if p < 1.0 and gs.size > k:
+    if p < 1.0:
+        # the kept mass reaches p (a row at the Top-k floor too: the floor
+        # only wins when the top k already reach p) ...
         if mass < p - MASS_WINDOW:
             return None
-        if mass - pin.min() >= p + MASS_WINDOW:
+        # ... and, above the floor, no smaller prefix would
+        if gs.size > k and mass - pin.min() >= p + MASS_WINDOW:
             return None
-    elif p >= 1.0 and gs.size != nb:
+    elif gs.size != nb:
         return None
     return "count" if gs.size != len(os_) else "order"
 
