@@ -142,10 +142,9 @@ def timed_step(path, q, k, v, out, p, kf, tm: StageTimer | None, balanced=True,
     if tm: tm.mark("s3")
     path.schedule()
     if tm: tm.mark("s4")
-    path.attend(balanced=balanced, runtime=runtime)
+    # the attention kernel stores O straight back in token order
+    path.attend(balanced=balanced, runtime=runtime, out=out)
     if tm: tm.mark("s5")
-    path.to_tokens(out)
-    if tm: tm.mark("s6")
 
 
 def run_steps(path, q, k, v, out, p, kf, steps, warmup, balanced=True, runtime=True):
@@ -158,10 +157,10 @@ def run_steps(path, q, k, v, out, p, kf, steps, warmup, balanced=True, runtime=T
         timed_step(path, q, k, v, out, p, kf, tm, balanced, runtime)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    names = ["hilbert", "permute_in", "route", "schedule", "attention", "permute_out"]
+    names = ["hilbert", "permute_in", "route", "schedule", "attention"]
     stages = {nm: float(np.mean(tm.durations(f"s{i}", f"s{i + 1}")))
               for i, nm in enumerate(names)}
-    step_ms = float(np.mean(tm.durations("s0", "s6")))
+    step_ms = float(np.mean(tm.durations("s0", "s5")))
     return wall * 1e3, step_ms, stages
 
 

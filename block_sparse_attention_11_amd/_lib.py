@@ -58,7 +58,8 @@ _SIGNATURES = {
     "fvattn_sparse_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_int, _c_float, _c_void_p, _c_void_p, _c_void_p,
-                                    _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p]),
+                                    _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_void_p]),
 }
 
 
@@ -216,10 +217,11 @@ def schedule(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
 
 def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
                 worker_tiles=None, n_workers: int = 0, timing=None, scale: float = 0.0,
-                v_tiles: bool = False, group: int = 1, claims=None):
+                v_tiles: bool = False, group: int = 1, claims=None, out_rows=None):
     """v is [H, n, d] (v_tiles=False) or [H, nB, d, block] tiles (v_tiles=True).
     claims: optional int32 [n_workers] scratch that turns on run-time
-    balancing of the persistent launch (reset by the call)."""
+    balancing of the persistent launch (reset by the call).
+    out_rows: optional int32 [n]; result row r goes to row out_rows[r] of o."""
     _dev(q, k, v, o, kv_count, kv_index)
     _need(q.shape == k.shape == o.shape and q.dim() == 3, "q,k,o [H, n, d]")
     _need(q.dtype == k.dtype == v.dtype == o.dtype, "one dtype")
@@ -237,6 +239,9 @@ def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
         _dev(timing)
         _need(timing.numel() == 4 * n_workers and timing.element_size() == 8,
               "timing u64[W][4]")
+    if out_rows is not None:
+        _dev(out_rows)
+        _need(out_rows.numel() == n and out_rows.dtype == torch.int32, "out_rows i32[n]")
     if claims is not None:
         _dev(claims)
         _need(claims.numel() == n_workers and claims.dtype == torch.int32, "claims i32[W]")
@@ -244,7 +249,7 @@ def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), H, n, d, block,
         V_TILES if v_tiles else V_ROWS, int(group), float(scale), _ptr(kv_count),
         _ptr(kv_index), _ptr(worker_offsets), _ptr(worker_tiles), int(n_workers),
-        _ptr(timing), _ptr(claims), _stream(q)))
+        _ptr(timing), _ptr(claims), _ptr(out_rows), _stream(q)))
 
 
 def attn_workers(dtype: torch.dtype, d: int, block: int, v_tiles: bool,

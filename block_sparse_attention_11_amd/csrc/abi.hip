@@ -128,7 +128,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
                        const int32_t* kv_count, const int32_t* kv_index,
                        const int32_t* worker_offsets, const int32_t* worker_tiles,
                        int n_workers, uint64_t* timing, int32_t* claims,
-                       hipStream_t stream) {
+                       const int32_t* out_rows, hipStream_t stream) {
   if (!q || !k || !v || !o || !kv_count || !kv_index) return FVATTN_EINVAL;
   if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
   if (isnan(scale) || isinf(scale)) return FVATTN_EINVAL;
@@ -168,6 +168,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   a.n_workers = worker_offsets ? n_workers : 0;
   a.timing = timing;
   a.claims = claims;
+  a.out_rows = out_rows;
   a.v_tiles = v_layout == FVATTN_V_TILES;
   a.group = group;
   a.tiles_per_head = (int)((nb + group - 1) / group);

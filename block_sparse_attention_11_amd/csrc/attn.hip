@@ -108,6 +108,12 @@ __device__ inline void keep_branch() { asm volatile(""); }
 // ---------------------------------------------------------------------------
 constexpr int kSimpleThreads = 256;
 constexpr float kRescaleSlack = 8.0f;
+
+// the row of o that result row r goes to: the caller's scatter (for instance
+// back to token order) or r itself
+__device__ inline int out_row(const AttnArgs& a, int r) {
+  return a.out_rows ? a.out_rows[r] : r;
+}
 constexpr int kSimpleChunk = 32;
 
 template <typename T, int DMAX, bool PERSIST>
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(kSimpleThreads) void attn_simple_kernel(AttnArgs a)
       const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
       for (int c = 0; c < DMAX; ++c)
-        if (c < d) store_elem(O + (hb + r) * d + c, acc[c] * inv);
+        if (c < d) store_elem(O + (hb + out_row(a, r)) * d + c, acc[c] * inv);
     }
     }  // q-blocks of the tile
   }
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(2 * BLK) void attn_mfma_kernel(AttnArgs a) {
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qvalid) {
-      uint16_t* orow = O + (hb + qrow) * D;
+      uint16_t* orow = O + (hb + out_row(a, qrow)) * D;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -559,7 +565,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
     const int hh = tile / nb, ii = tile - hh * nb;
     const int qr = ii * BLK + wave * 32 + col;
     if (qr < n) {
-      uint16_t* orow = O + ((size_t)hh * n + qr) * D;
+      uint16_t* orow = O + ((size_t)hh * n + out_row(a, qr)) * D;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -709,7 +715,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       const int qrow = i * BLK + wave * 32 + col;
       if (qrow < n) {
-        uint16_t* orow = O + ((size_t)h * n + qrow) * D;
+        uint16_t* orow = O + ((size_t)h * n + out_row(a, qrow)) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -838,7 +844,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   auto zero_rows = [&](int h, int i) {
     const int qr = i * BLK + wq * 32 + col;
     if (i < nb && qr < n) {
-      uint16_t* orow = O + ((size_t)h * n + qr) * D;
+      uint16_t* orow = O + ((size_t)h * n + out_row(a, qr)) * D;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -915,7 +921,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
       for (int r = lane; r < 2 * BLK; r += 64) {
         const int qr = i0 * BLK + r;
         if (qr < n) {
-          u32x4* orow = reinterpret_cast<u32x4*>(O + ((size_t)h * n + qr) * D);
+          u32x4* orow = reinterpret_cast<u32x4*>(O + ((size_t)h * n + out_row(a, qr)) * D);
 #pragma unroll
           for (int c = 0; c < D / 8; ++c) orow[c] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -1006,7 +1012,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (i < nb && qr < n) {
-      uint16_t* orow = O + ((size_t)w.h * n + qr) * D;
+      uint16_t* orow = O + ((size_t)w.h * n + out_row(a, qr)) * D;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll

@@ -76,6 +76,7 @@ struct AttnArgs {
   int n_workers;
   uint64_t* timing;               // null or [n_workers][4]
   int32_t* claims;                // null or [n_workers] claim counters (run-time balancing)
+  const int32_t* out_rows;        // null or [n]: result row r is stored at row out_rows[r]
   bool v_tiles;                   // V as [heads][nb][d][block] transposed tiles
   int group;                      // q-blocks per tile (1 or 2)
   int tiles_per_head;             // ceil(nb / group)

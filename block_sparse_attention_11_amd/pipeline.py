@@ -107,19 +107,26 @@ class FVAttnPath:
                       tile_order=self.tile_order, group=self.group,
                       worker_groups=self.worker_groups)
 
-    def attend(self, balanced: bool = True, timing: bool = True, runtime: bool = True):
+    def attend(self, balanced: bool = True, timing: bool = True, runtime: bool = True,
+               out=None):
         """balanced: persistent launch over the LPT lists (else the head-major
-        grid control); runtime: with run-time claims on top of the lists."""
+        grid control); runtime: with run-time claims on top of the lists.
+        out: write O straight into `out` in token order (the kernels scatter
+        rows through the Hilbert order); None: O stays in Hilbert order in
+        self.oh."""
+        o = self.oh if out is None else out
+        rows = None if out is None else self.perm
         if balanced:
-            _lib.sparse_attn(self.qh, self.kh, self.vh, self.oh, self.block,
+            _lib.sparse_attn(self.qh, self.kh, self.vh, o, self.block,
                              self.kv_count, self.kv_index, self.worker_offsets,
                              self.worker_tiles, self.n_workers,
                              self.timing if timing else None, v_tiles=self.v_tiles,
-                             group=self.group, claims=self.claims if runtime else None)
+                             group=self.group, claims=self.claims if runtime else None,
+                             out_rows=rows)
         else:
-            _lib.sparse_attn(self.qh, self.kh, self.vh, self.oh, self.block,
+            _lib.sparse_attn(self.qh, self.kh, self.vh, o, self.block,
                              self.kv_count, self.kv_index, v_tiles=self.v_tiles,
-                             group=self.group)
+                             group=self.group, out_rows=rows)
 
     def to_tokens(self, out):
         _lib.permute_rows(self.oh, out, self.inv_perm)
@@ -134,6 +141,5 @@ class FVAttnPath:
         self.to_hilbert(q, k, v)
         self.route(p, k_floor)
         self.schedule()
-        self.attend(balanced, runtime=runtime)
-        self.to_tokens(out)
+        self.attend(balanced, runtime=runtime, out=out)
         return out

@@ -246,6 +246,11 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
  *   output is the same bits as without claims.  Honoured by the q-block-pair
  *   kernel (group 2, FVATTN_V_TILES, an MFMA shape); the other kernels run
  *   their lists as given.
+ * out_rows (nullable, device int32 [n]): result row r of every head is stored
+ *   at row out_rows[r] of o instead of row r; passing the Hilbert order `perm`
+ *   of fvattn_hilbert_permute writes O straight back in token order, which
+ *   saves the separate inverse permute pass.  Must hold distinct rows in
+ *   [0, n) (rows written twice race; out-of-range rows are not checked).
  * Kernels: bf16 with (d, block) in {(64, 64), (128, 128), (64, 128),
  * (128, 64)} runs on an MFMA kernel (the LDS-DMA ones for FVATTN_V_TILES);
  * every other (dtype, d <= 128, block <= 256) combination runs on a plain
@@ -257,7 +262,8 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o,
                        const int32_t* kv_count,
                        const int32_t* kv_index, const int32_t* worker_offsets,
                        const int32_t* worker_tiles, int n_workers,
-                       uint64_t* timing, int32_t* claims, hipStream_t stream);
+                       uint64_t* timing, int32_t* claims, const int32_t* out_rows,
+                       hipStream_t stream);
 
 /*
  * Persistent workers for fvattn_sparse_attn on the current device: the

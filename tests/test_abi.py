@@ -95,22 +95,22 @@ def _validation_main():
         (lib.fvattn_schedule(P, 40, 591, 1, 4, 8 << 8, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule(P, 4097, 2, 1, 256, 8 << 8, P, P, P, P, P, 1 << 30, N), EUNS),
         # attention
-        (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 256, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N), EUNS),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, float("inf"), P, P, N, N, 0, N, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, N, 4, N, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, P, 0, N, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, P, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 256, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N, N), EUNS),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, float("inf"), P, P, N, N, 0, N, N, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, N, 4, N, N, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, P, 0, N, N, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, P, N, N, N), EINVAL),
         # run-time claims need the persistent launch
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, P, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 2, 1, 0.0, P, P, N, N, 0, N, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, P, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 2, 1, 0.0, P, P, N, N, 0, N, N, N, N), EINVAL),
         # workers
         (lib.fvattn_attn_workers(1, 128, 128, 1, 2, N), EINVAL),
         (lib.fvattn_attn_workers(1, 128, 128, 1, 3, ctypes.byref(ctypes.c_int())), EINVAL),
         (lib.fvattn_attn_workers(1, 128, 128, 5, 1, ctypes.byref(ctypes.c_int())), EINVAL),
         (lib.fvattn_schedule(P, 40, 591, 3, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 1, 3, 0.0, P, P, N, N, 0, N, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 1, 3, 0.0, P, P, N, N, 0, N, N, N, N), EINVAL),
         # pack_v
         (lib.fvattn_pack_v(P, P, P, 1, 128, 64, 16, 1, N), EINVAL),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 16, 0, N), EUNS),
@@ -119,7 +119,7 @@ def _validation_main():
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 12, 1, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 8, 1, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 24, 1, N), EUNS),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 12, 1, 1, 0.0, P, P, N, N, 0, N, N, N), EUNS),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 12, 1, 1, 0.0, P, P, N, N, 0, N, N, N, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), N, 1, 128, 64, 16, 1, N), EINVAL),
     ]
     bad = [(i, got, want) for i, (got, want) in enumerate(checks) if got != want]

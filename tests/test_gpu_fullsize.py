@@ -103,13 +103,12 @@ def check_attention(path, w, v, out, tiles):
     perm = path.perm.cpu().numpy()
     gc = path.kv_count.cpu().numpy()
     gi = path.kv_index.cpu().numpy()
-    oh = path.oh
     worst = {"max_abs": 0.0, "rel_l2": 0.0}
     for h in sorted({t[0] for t in tiles}):
         qh, kh = head_f64(path.qh, h)[None], head_f64(path.kh, h)[None]
         vh = ort.permute_rows(head_f64(v, h)[None], perm)
-        ohh = oh[h].float().cpu().numpy()
         outh = out[h].float().cpu().numpy()
+        ohh = outh[perm]                    # Hilbert order
         for (hh, i) in tiles:
             if hh != h:
                 continue
@@ -122,8 +121,6 @@ def check_attention(path, w, v, out, tiles):
             tol = TOL[w.dtype]
             assert err["max_abs"] <= tol["max_abs"] and err["rel_l2"] <= tol["rel_l2"], \
                 (h, i, int(gc[h, i]), err)
-            # the token-order output holds the same rows
-            assert np.array_equal(outh[perm[r0:r1]], ohh[r0:r1])
     say(f"  attention on {len(tiles)} sampled tiles: worst {worst}")
 
 
