@@ -103,6 +103,14 @@ __device__ inline void store_elem<bf16s>(bf16s* p, float v) {
 // rescale) into unconditional selects executed on every block.
 __device__ inline void keep_branch() { asm volatile(""); }
 
+// max of v over lanes l and l ^ 32 (the two halves of a wavefront), with one
+// VALU lane swap instead of a round trip through LDS
+__device__ inline float max_with_other_half(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                   false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
 // ---------------------------------------------------------------------------
 // Plain fp32 kernel.
 // ---------------------------------------------------------------------------
@@ -1063,6 +1071,21 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
                                                             qf[kk], s[kt], 0, 0, 0);
           }
         }
+        if (half == 0) {
+          // the first half starts right after the barrier with nothing else
+          // to overlap: keep kReadAhead K reads in flight ahead of the MFMAs
+          // (the default schedule waits on every second read)
+          constexpr int kReadAhead = 6;
+          constexpr int kN = (D / 16) * KT;
+          static_assert(kN > kReadAhead, "read-ahead depth");
+          __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);   // LDS reads
+#pragma unroll
+          for (int x = 0; x < kN - kReadAhead; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // one read
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
+        }
         if (r0 + half * HK + HK > n) {
           keep_branch();
 #pragma unroll
@@ -1078,7 +1101,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = max_with_other_half(mx);
         const float mxs = mx * sl2;
         const bool grow = mxs > m_run + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(grow)) {
