@@ -33,6 +33,7 @@ _c_void_p = ctypes.c_void_p
 _c_int = ctypes.c_int
 _c_float = ctypes.c_float
 _c_size_t = ctypes.c_size_t
+_c_double = ctypes.c_double
 
 _SIGNATURES = {
     "fvattn_status_string": (ctypes.c_char_p, [_c_int]),
@@ -58,8 +59,19 @@ _SIGNATURES = {
     "fvattn_sparse_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_int, _c_float, _c_void_p, _c_void_p, _c_void_p,
-                                    _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p,
-                                    _c_void_p]),
+                                    _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
+                                    _c_void_p, _c_void_p]),
+    "fvattn_schedule_heads": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p,
+                                       _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "fvattn_sasa_plan": (_c_int, [_c_void_p, _c_int, _c_int, _c_double, _c_double,
+                                  _c_double, _c_double, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p]),
+    "fvattn_sasa_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
+    "fvattn_sasa_augment": (_c_int, [_c_void_p, _c_size_t, _c_int, _c_int, _c_int, _c_int,
+                                     _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                     _c_size_t, _c_void_p]),
 }
 
 
@@ -217,10 +229,12 @@ def schedule(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
 
 def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
                 worker_tiles=None, n_workers: int = 0, timing=None, scale: float = 0.0,
-                v_tiles: bool = False, group: int = 1, claims=None, out_rows=None):
+                v_tiles: bool = False, group: int = 1, claims=None, out_rows=None,
+                claim_groups: int = 0):
     """v is [H, n, d] (v_tiles=False) or [H, nB, d, block] tiles (v_tiles=True).
     claims: optional int32 [n_workers] scratch that turns on run-time
-    balancing of the persistent launch (reset by the call).
+    balancing of the persistent launch (reset by the call); claim_groups > 1
+    keeps every claim inside the workgroup's own group w % claim_groups.
     out_rows: optional int32 [n]; result row r goes to row out_rows[r] of o."""
     _dev(q, k, v, o, kv_count, kv_index)
     _need(q.shape == k.shape == o.shape and q.dim() == 3, "q,k,o [H, n, d]")
@@ -249,7 +263,76 @@ def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), H, n, d, block,
         V_TILES if v_tiles else V_ROWS, int(group), float(scale), _ptr(kv_count),
         _ptr(kv_index), _ptr(worker_offsets), _ptr(worker_tiles), int(n_workers),
-        _ptr(timing), _ptr(claims), _ptr(out_rows), _stream(q)))
+        _ptr(timing), _ptr(claims), int(claim_groups), _ptr(out_rows), _stream(q)))
+
+
+def schedule_heads(kv_count, n_workers: int, head_group, n_groups: int, lpt_order,
+                   worker_offsets, worker_tiles, worker_load, workspace,
+                   tile_order: bool = False, group: int = 1):
+    """Two-level LPT with the head -> group map given (int32 [H])."""
+    _dev(kv_count, head_group, lpt_order, worker_offsets, worker_tiles, worker_load,
+         workspace)
+    _need(kv_count.dim() == 2 and kv_count.dtype == torch.int32, "kv_count i32[H, nB]")
+    H, nb = kv_count.shape
+    tiles = H * ((nb + group - 1) // group)
+    _need(head_group.numel() == H and head_group.dtype == torch.int32, "head_group i32[H]")
+    _need(lpt_order.numel() == tiles and worker_tiles.numel() == tiles, "tile arrays")
+    _need(worker_offsets.numel() == n_workers + 1, "worker_offsets[W+1]")
+    _need(worker_load.numel() == n_workers and worker_load.dtype == torch.int64,
+          "worker_load i64[W]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("fvattn_schedule_heads", load_library().fvattn_schedule_heads(
+        _ptr(kv_count), H, nb, int(group), int(n_workers), int(n_groups), _ptr(head_group),
+        SCHED_TILE_ORDER if tile_order else 0, _ptr(lpt_order), _ptr(worker_offsets),
+        _ptr(worker_tiles), _ptr(worker_load), _ptr(workspace), ws_bytes,
+        _stream(kv_count)))
+
+
+# the pages' SASA / RLB constants
+SASA_K1, SASA_K2, SASA_N1, SASA_N2 = 1.05, 1.10, 0.8, 0.07
+
+
+def sasa_plan(head_load, n_groups: int, head_group, group_budget, info,
+              k1: float = SASA_K1, k2: float = SASA_K2, n1: float = SASA_N1,
+              n2: float = SASA_N2):
+    """Mode, head moves and per-group budgets (device outputs)."""
+    _dev(head_load, head_group, group_budget, info)
+    H = head_load.numel()
+    _need(head_load.dtype == torch.int64, "head_load i64[H]")
+    _need(head_group.numel() == H and head_group.dtype == torch.int32, "head_group i32[H]")
+    _need(group_budget.numel() == n_groups and group_budget.dtype == torch.int64,
+          "group_budget i64[G]")
+    _need(info.numel() == 2 + 2 * n_groups and info.dtype == torch.int64, "info i64[2+2G]")
+    _check("fvattn_sasa_plan", load_library().fvattn_sasa_plan(
+        _ptr(head_load), H, int(n_groups), float(k1), float(k2), float(n1), float(n2),
+        _ptr(head_group), _ptr(group_budget), _ptr(info), _stream(head_load)))
+
+
+def sasa_workspace_size(heads: int, n: int, block: int, n_groups: int) -> int:
+    return int(load_library().fvattn_sasa_workspace_size(heads, n, block, n_groups))
+
+
+def sasa_augment(route_workspace, heads: int, n: int, d: int, block: int, head_group,
+                 group_budget, mask, kv_count, kv_index, head_load, head_density, added,
+                 workspace):
+    """Adds each group's budget of skipped blocks, most important first, and
+    rewrites the routing outputs (route_workspace: that of the route call)."""
+    _dev(route_workspace, head_group, group_budget, mask, kv_count, kv_index, head_load,
+         head_density, added, workspace)
+    G = group_budget.numel()
+    nb = (n + block - 1) // block
+    _need(mask.dtype == torch.uint8 and mask.numel() == heads * nb * nb, "mask u8[H,nB,nB]")
+    _need(kv_count.dtype == torch.int32 and kv_count.numel() == heads * nb, "kv_count")
+    _need(kv_index.dtype == torch.int32 and kv_index.numel() == heads * nb * nb, "kv_index")
+    _need(head_group.numel() == heads and head_group.dtype == torch.int32, "head_group")
+    _need(group_budget.dtype == torch.int64 and added.dtype == torch.int64 and
+          added.numel() == G, "budget / added i64[G]")
+    _check("fvattn_sasa_augment", load_library().fvattn_sasa_augment(
+        _ptr(route_workspace), route_workspace.numel() * route_workspace.element_size(),
+        int(heads), int(n), int(d), int(block), _ptr(head_group), _ptr(group_budget), G,
+        _ptr(mask), _ptr(kv_count), _ptr(kv_index), _ptr(head_load), _ptr(head_density),
+        _ptr(added), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(mask)))
 
 
 def attn_workers(dtype: torch.dtype, d: int, block: int, v_tiles: bool,

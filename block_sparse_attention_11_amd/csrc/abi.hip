@@ -118,8 +118,76 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group
   if (!workspace || workspace_bytes < need) return FVATTN_EWORKSPACE;
   return launch_status(fvattn::launch_schedule(
       kv_count, heads, n_qblocks, group, n_workers, n_groups > 1 ? n_groups : 1,
-      (flags & FVATTN_SCHED_TILE_ORDER) != 0,
+      (flags & FVATTN_SCHED_TILE_ORDER) != 0, nullptr,
       lpt_order, worker_offsets, worker_tiles, worker_load, workspace, stream));
+}
+
+int fvattn_schedule_heads(const int32_t* kv_count, int heads, int n_qblocks, int group,
+                          int n_workers, int n_groups, const int32_t* head_group, int flags,
+                          int32_t* lpt_order, int32_t* worker_offsets, int32_t* worker_tiles,
+                          int64_t* worker_load, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (!kv_count || !head_group || !lpt_order || !worker_offsets || !worker_tiles ||
+      !worker_load)
+    return FVATTN_EINVAL;
+  if (heads < 1 || n_qblocks < 1 || n_workers < 1) return FVATTN_EINVAL;
+  if (group != 1 && group != 2) return FVATTN_EINVAL;
+  if (!fits_int32((long long)heads * n_qblocks)) return FVATTN_EINVAL;
+  if (flags & ~FVATTN_SCHED_TILE_ORDER) return FVATTN_EINVAL;
+  if (n_groups < 2 || n_groups > fvattn::schedule_max_groups() || n_groups > n_workers)
+    return FVATTN_EINVAL;
+  if (n_workers > fvattn::kMaxWorkers) return FVATTN_EUNSUPPORTED;
+  const size_t need = fvattn::schedule_workspace_bytes(heads, n_qblocks, n_workers);
+  if (!workspace || workspace_bytes < need) return FVATTN_EWORKSPACE;
+  return launch_status(fvattn::launch_schedule(
+      kv_count, heads, n_qblocks, group, n_workers, n_groups,
+      (flags & FVATTN_SCHED_TILE_ORDER) != 0, head_group,
+      lpt_order, worker_offsets, worker_tiles, worker_load, workspace, stream));
+}
+
+int fvattn_sasa_plan(const int64_t* head_load, int heads, int n_groups, double k1, double k2,
+                     double n1, double n2, int32_t* head_group, int64_t* group_budget,
+                     int64_t* info, hipStream_t stream) {
+  if (!head_load || !head_group || !group_budget || !info) return FVATTN_EINVAL;
+  if (heads < 1 || n_groups < 1) return FVATTN_EINVAL;
+  if (!(k1 >= 1.0) || !(k2 >= k1) || isinf(k2) || !(n1 >= 0.0) || !(n1 <= 1.0) ||
+      !(n2 >= 0.0) || !(n2 <= 1.0))
+    return FVATTN_EINVAL;
+  if (heads > fvattn::kMaxSasaHeads || n_groups > fvattn::kMaxSasaGroups)
+    return FVATTN_EUNSUPPORTED;
+  return launch_status(fvattn::launch_sasa_plan(head_load, heads, n_groups, k1, k2, n1, n2,
+                                                head_group, group_budget, info, stream));
+}
+
+size_t fvattn_sasa_workspace_size(int heads, int n, int block, int n_groups) {
+  if (heads < 1 || n < 1 || block < 1 || n_groups < 1) return 0;
+  return fvattn::sasa_workspace_bytes(heads, n, block, n_groups);
+}
+
+int fvattn_sasa_augment(const void* route_workspace, size_t route_workspace_bytes, int heads,
+                        int n, int d, int block, const int32_t* head_group,
+                        const int64_t* group_budget, int n_groups, uint8_t* mask,
+                        int32_t* kv_count, int32_t* kv_index, int64_t* head_load,
+                        float* head_density, int64_t* added, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  if (!route_workspace || !head_group || !group_budget || !mask || !kv_count || !kv_index ||
+      !head_load || !head_density || !added)
+    return FVATTN_EINVAL;
+  if (heads < 1 || n < 1 || d < 1 || block < 1 || n_groups < 1) return FVATTN_EINVAL;
+  if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
+  const int64_t nb = nblocks(n, block);
+  if (nb > 4096) return FVATTN_EUNSUPPORTED;
+  if (n_groups > fvattn::kMaxSasaGroups) return FVATTN_EUNSUPPORTED;
+  if (route_workspace_bytes < fvattn::route_workspace_bytes(heads, n, d, block))
+    return FVATTN_EWORKSPACE;
+  const size_t need = fvattn::sasa_workspace_bytes(heads, n, block, n_groups);
+  if (!workspace || workspace_bytes < need) return FVATTN_EWORKSPACE;
+  const fvattn::RouteWorkspace rw =
+      fvattn::route_carve(const_cast<void*>(route_workspace), heads, n, d, block);
+  return launch_status(fvattn::launch_sasa_augment(rw.z, heads, n, block, head_group,
+                                                   group_budget, n_groups, mask, kv_count,
+                                                   kv_index, head_load, head_density, added,
+                                                   workspace, stream));
 }
 
 int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int dtype,
@@ -127,7 +195,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
                        float scale,
                        const int32_t* kv_count, const int32_t* kv_index,
                        const int32_t* worker_offsets, const int32_t* worker_tiles,
-                       int n_workers, uint64_t* timing, int32_t* claims,
+                       int n_workers, uint64_t* timing, int32_t* claims, int claim_groups,
                        const int32_t* out_rows, hipStream_t stream) {
   if (!q || !k || !v || !o || !kv_count || !kv_index) return FVATTN_EINVAL;
   if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
@@ -149,6 +217,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
       ((long long)heads * nb * block * d * 2 > 0x7fffffffLL || block % 16 != 0))
     return FVATTN_EUNSUPPORTED;
   if ((timing || claims) && !worker_offsets) return FVATTN_EINVAL;
+  if (claim_groups < 0 || claim_groups > 64) return FVATTN_EINVAL;
   fvattn::AttnArgs a;
   a.q = q;
   a.k = k;
@@ -168,6 +237,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   a.n_workers = worker_offsets ? n_workers : 0;
   a.timing = timing;
   a.claims = claims;
+  a.claim_groups = claim_groups;
   a.out_rows = out_rows;
   a.v_tiles = v_layout == FVATTN_V_TILES;
   a.group = group;

@@ -863,8 +863,10 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   // Run-time balancing.  Counter claims[w] counts the tiles of worker w's
   // LPT list handed out so far.  A workgroup takes the next tile of its own
   // list while there is one, then the next tile of the list with the most
-  // tiles left; every hand-out is one atomic add, so each tile runs exactly
-  // once whichever workgroup runs it.  Wave 0 makes the claims, two tiles
+  // tiles left (with claim_groups = x > 1, only among the lists of its own
+  // group, w % x, so the groups stay independent like ranks); every hand-out
+  // is one atomic add, so each tile runs exactly once whichever workgroup
+  // runs it.  Wave 0 makes the claims, two tiles
   // ahead, and posts the list positions in an LDS ring; the other waves read
   // a slot at least one barrier after it was written.  Pairs with no kept
   // block are written as zeros by wave 0 while claiming.
@@ -889,7 +891,8 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
         for (int base = 0; base < W; base += 64) {
           const int v = base + lane;
           int rem = 0;
-          if (v < W && v != own) {
+          const int X = a.claim_groups;
+          if (v < W && v != own && (X <= 1 || v % X == own % X)) {
             const int lo = a.worker_offsets[v], hi = a.worker_offsets[v + 1];
             rem = hi - lo - __hip_atomic_load(a.claims + v, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);

@@ -48,14 +48,20 @@ hipError_t launch_route(const void* q, const void* k, bool bf16, int heads,
                         uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
                         int64_t* head_load, float* head_density,
                         const RouteWorkspace& ws, hipStream_t s);
+// per-head sum of kv_count (int64) and density = sum / nB^2
+hipError_t launch_head_load(const int32_t* kv_count, int heads, int nb, int64_t* head_load,
+                            float* head_density, hipStream_t s);
 
 // ---- schedule.hip ----------------------------------------------------------
 constexpr int kMaxWorkers = 2048;
 constexpr int kMaxCost = 65535;
 size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers);
 // tiles = heads * ceil(n_qblocks / group); tile t = h * ceil(nq/group) + m
+// head_group (nullable, n_groups > 1): the group of every head, used as
+// given instead of the LPT grouping of the head loads
 hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group,
-                           int n_workers, int n_groups, bool tile_order, int32_t* lpt_order,
+                           int n_workers, int n_groups, bool tile_order,
+                           const int32_t* head_group, int32_t* lpt_order,
                            int32_t* worker_offsets, int32_t* worker_tiles,
                            int64_t* worker_load, void* ws, hipStream_t s);
 int schedule_max_groups();
@@ -76,6 +82,7 @@ struct AttnArgs {
   int n_workers;
   uint64_t* timing;               // null or [n_workers][4]
   int32_t* claims;                // null or [n_workers] claim counters (run-time balancing)
+  int claim_groups;               // > 1: claims only from lists w' with w' % x == w % x
   const int32_t* out_rows;        // null or [n]: result row r is stored at row out_rows[r]
   bool v_tiles;                   // V as [heads][nb][d][block] transposed tiles
   int group;                      // q-blocks per tile (1 or 2)
@@ -86,5 +93,20 @@ bool attn_has_mfma_instance(bool bf16, int d, int block);
 hipError_t attn_occupancy(bool bf16, int d, int block, bool v_tiles, int group,
                           int* per_cu);
 hipError_t launch_sparse_attn(const AttnArgs& a, bool bf16, hipStream_t s);
+
+// ---- sasa.hip --------------------------------------------------------------
+constexpr int kMaxSasaHeads = 4096;
+constexpr int kMaxSasaGroups = 64;
+size_t sasa_workspace_bytes(int heads, int n, int block, int groups);
+// info: int64 [2 + 2 * groups] = mode, moves, group loads before, after
+hipError_t launch_sasa_plan(const int64_t* head_load, int heads, int groups, double k1,
+                            double k2, double n1, double n2, int32_t* head_group,
+                            int64_t* budget, int64_t* info, hipStream_t s);
+// z: the routing scores [heads][nB][nB] left by launch_route for the same inputs
+hipError_t launch_sasa_augment(const float* z, int heads, int n, int block,
+                               const int32_t* head_group, const int64_t* budget, int groups,
+                               uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
+                               int64_t* head_load, float* head_density, int64_t* added,
+                               void* ws, hipStream_t s);
 
 }  // namespace fvattn

@@ -298,6 +298,13 @@ RouteWorkspace route_carve(void* ws, int heads, int n, int d, int block) {
   return w;
 }
 
+hipError_t launch_head_load(const int32_t* kv_count, int heads, int nb, int64_t* head_load,
+                            float* head_density, hipStream_t s) {
+  hipLaunchKernelGGL(load_kernel, dim3(heads), dim3(256), 0, s, kv_count, nb, head_load,
+                     head_density);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const void* q, const void* k, bool bf16, int heads,
                         int n, int d, int block, float p, int k_floor,
                         uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
@@ -328,9 +335,7 @@ hipError_t launch_route(const void* q, const void* k, bool bf16, int heads,
                      ws.z, nb, np, p, k_floor, mask, kv_count, kv_index);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(load_kernel, dim3(heads), dim3(256), 0, s, kv_count, nb,
-                     head_load, head_density);
-  return hipGetLastError();
+  return launch_head_load(kv_count, heads, nb, head_load, head_density, s);
 }
 
 }  // namespace fvattn

@@ -323,6 +323,13 @@ __global__ __launch_bounds__(kAssignThreads) void lpt_assign_kernel(
 // (lane x holds group x's load; every head goes to the least-loaded group,
 // lowest index on ties).
 constexpr int kMaxGroupHeads = 4096;
+// a caller's head -> group map, clamped to [0, n_groups)
+__global__ void head_group_copy_kernel(const int32_t* __restrict__ in, int heads, int n_groups,
+                                       int32_t* __restrict__ out) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h < heads) out[h] = min(max(in[h], 0), n_groups - 1);
+}
+
 __global__ __launch_bounds__(1024) void head_group_kernel(
     const int32_t* __restrict__ cost, int heads, int tph, int n_groups,
     int32_t* __restrict__ head_group) {
@@ -468,7 +475,8 @@ int schedule_max_groups() { return kMaxGroups; }
 int schedule_max_group_heads() { return kMaxGroupHeads; }
 
 hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group,
-                           int n_workers, int n_groups, bool tile_order, int32_t* lpt_order,
+                           int n_workers, int n_groups, bool tile_order,
+                           const int32_t* head_group, int32_t* lpt_order,
                            int32_t* worker_offsets, int32_t* worker_tiles,
                            int64_t* worker_load, void* wsp, hipStream_t s) {
   const int per_head = (n_qblocks + group - 1) / group;
@@ -489,8 +497,13 @@ hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, in
   const int X = min(n_groups, n_workers);
   const int32_t* seq = lpt_order;
   if (X > 1) {
-    hipLaunchKernelGGL(head_group_kernel, dim3(1), dim3(1024), 0, s, cost, heads, per_head, X,
-                       ws.head_group);
+    if (head_group) {
+      hipLaunchKernelGGL(head_group_copy_kernel, dim3((heads + 255) / 256), dim3(256), 0, s,
+                         head_group, heads, X, ws.head_group);
+    } else {
+      hipLaunchKernelGGL(head_group_kernel, dim3(1), dim3(1024), 0, s, cost, heads, per_head, X,
+                         ws.head_group);
+    }
     hipLaunchKernelGGL(group_partition_kernel, dim3(1), dim3(kPartThreads), 0, s, lpt_order,
                        tiles, per_head, ws.head_group, X, ws.gseq, ws.goff);
     hipLaunchKernelGGL(lpt_assign_kernel, dim3(X), dim3(kAssignThreads), 0, s, cost, ws.gseq,

@@ -7,9 +7,18 @@ library:
     permute_rows     Q, K -> Hilbert order
     pack_v           V -> Hilbert order, one transposed tile per key block
     route            pooled-Q/K Top-p + Top-k -> mask, kept lists, head load
+    [sasa_plan, sasa_augment   per-rank image only: head moves and extra
+                     blocks on the groups off the critical path]
     schedule         LPT work list over (head, q-block) tiles
-    sparse_attn      persistent block-sparse attention over the kept blocks
-    permute_rows     O -> token order
+    sparse_attn      persistent block-sparse attention over the kept blocks,
+                     storing O straight back in token order
+
+With ranks = G > 1 the path runs the per-rank image of the pages' system:
+the persistent workers form G groups (worker w in group w % G; G = 8 puts
+one group on each XCD), heads start in contiguous shards, the SASA plan may
+move heads between groups (RLB) and, with sasa=True, adds each group's
+budget of skipped high-importance blocks; every group then claims work only
+from its own lists, so the groups finish independently, like ranks.
 """
 from __future__ import annotations
 
@@ -32,7 +41,7 @@ class FVAttnPath:
     def __init__(self, heads: int, grid, d: int, block: int, dtype=torch.bfloat16,
                  n_workers: int | None = None, device="cuda", tile_order: bool = False,
                  v_tiles: bool | None = None, group: int | None = None,
-                 worker_groups: int | None = None):
+                 worker_groups: int | None = None, ranks: int = 0, sasa: bool = False):
         self.heads, self.grid, self.d, self.block = heads, tuple(grid), d, block
         T, Y, X = self.grid
         self.n = T * Y * X
@@ -82,6 +91,20 @@ class FVAttnPath:
         self.timing = torch.zeros((W, 4), dtype=torch.int64, device=dev)
         # claim counters for run-time balancing of the persistent launch
         self.claims = torch.zeros(W, dtype=torch.int32, device=dev)
+        # per-rank image (SASA / RLB on the worker groups)
+        if sasa and ranks < 2:
+            raise ValueError("sasa needs ranks >= 2 (the per-rank image)")
+        if ranks > 1 and (ranks > min(64, W) or W % ranks != 0):
+            raise ValueError("ranks must divide the worker count and be <= 64")
+        self.ranks, self.sasa = ranks, sasa
+        if ranks > 1:
+            i64 = dict(dtype=torch.int64, device=dev)
+            self.head_group = torch.empty(H, **i32)
+            self.group_budget = torch.empty(ranks, **i64)
+            self.sasa_info = torch.empty(2 + 2 * ranks, **i64)
+            self.sasa_added = torch.zeros(ranks, **i64)
+            self.sasa_ws = torch.empty(_lib.sasa_workspace_size(H, n, block, ranks),
+                                       dtype=torch.uint8, device=dev)
         self.ordered = False
 
     # -- steps -------------------------------------------------------------
@@ -101,7 +124,24 @@ class FVAttnPath:
         _lib.route(self.qh, self.kh, self.block, p, k_floor, self.mask, self.kv_count,
                    self.kv_index, self.head_load, self.head_density, self.route_ws)
 
+    def plan_ranks(self):
+        """Per-rank image: mode, head moves and budgets; with sasa, the extra
+        blocks (rewrites mask, kv lists, head load and density)."""
+        _lib.sasa_plan(self.head_load, self.ranks, self.head_group, self.group_budget,
+                       self.sasa_info)
+        if self.sasa:
+            _lib.sasa_augment(self.route_ws, self.heads, self.n, self.d, self.block,
+                              self.head_group, self.group_budget, self.mask, self.kv_count,
+                              self.kv_index, self.head_load, self.head_density,
+                              self.sasa_added, self.sasa_ws)
+
     def schedule(self):
+        if self.ranks > 1:
+            _lib.schedule_heads(self.kv_count, self.n_workers, self.head_group, self.ranks,
+                                self.lpt_order, self.worker_offsets, self.worker_tiles,
+                                self.worker_load, self.sched_ws,
+                                tile_order=self.tile_order, group=self.group)
+            return
         _lib.schedule(self.kv_count, self.n_workers, self.lpt_order, self.worker_offsets,
                       self.worker_tiles, self.worker_load, self.sched_ws,
                       tile_order=self.tile_order, group=self.group,
@@ -122,7 +162,8 @@ class FVAttnPath:
                              self.worker_tiles, self.n_workers,
                              self.timing if timing else None, v_tiles=self.v_tiles,
                              group=self.group, claims=self.claims if runtime else None,
-                             out_rows=rows)
+                             out_rows=rows,
+                             claim_groups=self.ranks if self.ranks > 1 else 0)
         else:
             _lib.sparse_attn(self.qh, self.kh, self.vh, o, self.block,
                              self.kv_count, self.kv_index, v_tiles=self.v_tiles,
@@ -140,6 +181,8 @@ class FVAttnPath:
             self.order()
         self.to_hilbert(q, k, v)
         self.route(p, k_floor)
+        if self.ranks > 1:
+            self.plan_ranks()
         self.schedule()
         self.attend(balanced, runtime=runtime, out=out)
         return out

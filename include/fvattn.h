@@ -206,6 +206,93 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Two-level LPT with the head -> group map given: as fvattn_schedule with
+ * FVATTN_SCHED_GROUPS(n_groups), except that head h belongs to group
+ * head_group[h] (device int32 [heads], values clamped to [0, n_groups))
+ * instead of the LPT grouping of the head loads.  This is the schedule of
+ * the per-rank image of fvattn_sasa_plan (groups = ranks, heads sharded,
+ * then moved by the plan).  flags: 0 or FVATTN_SCHED_TILE_ORDER;
+ * 2 <= n_groups <= min(64, n_workers).  Other limits, outputs, workspace and
+ * errors as fvattn_schedule.  Bit-exact.
+ */
+int fvattn_schedule_heads(const int32_t* kv_count, int heads, int n_qblocks,
+                          int group, int n_workers, int n_groups,
+                          const int32_t* head_group, int flags, int32_t* lpt_order,
+                          int32_t* worker_offsets, int32_t* worker_tiles,
+                          int64_t* worker_load, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Slack-aware sparse augmentation (SASA), planning step.
+ *
+ * Source: after balancing, ranks off the critical path wait for it; SASA
+ * spends that idle time on extra high-value blocks on those ranks only, and
+ * the imbalance factor selects the regime with thresholds k1 = 1.05 and
+ * k2 = 1.10 (nothing below k1, SASA alone below k2, runtime load balancing
+ * (RLB) and then SASA above), with an augmentation coefficient n1 = 0.8 and
+ * a trigger threshold n2 = 0.07; RLB moves at most one local head per rank
+ * (aixai.ru FVAttn post, sections "Runtime Load Balancing (RLB)" and
+ * "Slack-Aware Sparse Augmentation (SASA)"; PaperDaily FVAttn article, SASA
+ * paragraphs).  On one GPU the ranks are n_groups groups of persistent
+ * workers (worker w in group w % n_groups; 8 = one per XCD on MI355X):
+ *   start:  head h in group floor(h * n_groups / heads) (contiguous shards);
+ *   loads:  group load = sum of head_load over its heads (kept blocks);
+ *           rho = max / mean of the group loads (float64);
+ *   mode:   0 if rho < k1, 1 (SASA) if rho < k2, else 2 (RLB + SASA);
+ *   RLB (mode 2): while the critical group (largest load, lowest index) has
+ *           given no head, move its heaviest head not moved before (lowest
+ *           index on ties) with load > 0 and load_t + load_h < load_c to the
+ *           least-loaded group t (lowest index); stop when there is none;
+ *   budget (modes 1, 2): slack_g = max load - load_g; group_budget[g] =
+ *           floor(n1 * slack_g) if slack_g >= n2 * max load (float64), else 0.
+ * Inputs: head_load (device int64 [heads], as fvattn_route writes it).
+ * Outputs (device): head_group int32 [heads]; group_budget int64 [n_groups]
+ * (extra blocks per group); info int64 [2 + 2*n_groups] = mode, number of
+ * head moves, group loads before the moves, group loads after.
+ * Bit-exact (integer arithmetic and float64 comparisons).
+ * Errors: FVATTN_EINVAL for null pointers, heads or n_groups < 1, k1 < 1,
+ * k2 < k1 or infinite, n1 or n2 outside [0, 1]; FVATTN_EUNSUPPORTED for
+ * heads > 4096 or n_groups > 64.
+ */
+int fvattn_sasa_plan(const int64_t* head_load, int heads, int n_groups,
+                     double k1, double k2, double n1, double n2,
+                     int32_t* head_group, int64_t* group_budget, int64_t* info,
+                     hipStream_t stream);
+
+/*
+ * SASA augmentation: adds to the mask, for every group g with
+ * group_budget[g] > 0, the group_budget[g] blocks it skipped whose routing
+ * importance is largest (all of them if there are fewer), and rewrites the
+ * routing outputs to match.
+ *
+ * Source: the extra blocks come from the blocks the sparse mask skipped, in
+ * importance order, and the routing pass already gives that order (aixai.ru
+ * FVAttn post, sections "Sparse-routing frontend" and "Slack-Aware Sparse
+ * Augmentation (SASA)"; PaperDaily FVAttn article).  Importance of (h, i, j)
+ * = the routing softmax P[h][i][j] = exp(z - max z) / sum, recomputed in
+ * fp32 from the scores fvattn_route leaves in its workspace, with the
+ * routing pass's own arithmetic; blocks of a group are ranked by (P desc,
+ * h asc, i asc, j asc) over the group's heads (head_group[h]).
+ * route_workspace: the workspace of the fvattn_route call that produced
+ *   mask/kv_* for the same (heads, n, d, block), unchanged since.
+ * In/out (device): mask, kv_count, kv_index (ascending, as fvattn_route
+ *   writes them); head_load and head_density are recomputed for every head.
+ * Out: added int64 [n_groups], blocks added per group.
+ * workspace: at least fvattn_sasa_workspace_size(heads, n, block, n_groups).
+ * Errors: FVATTN_EINVAL for null pointers or bad sizes; FVATTN_EUNSUPPORTED
+ * for nB > 4096 or n_groups > 64; FVATTN_EWORKSPACE for a short workspace.
+ * Rows of groups without a budget are left untouched.
+ */
+size_t fvattn_sasa_workspace_size(int heads, int n, int block, int n_groups);
+int fvattn_sasa_augment(const void* route_workspace, size_t route_workspace_bytes,
+                        int heads, int n, int d, int block,
+                        const int32_t* head_group, const int64_t* group_budget,
+                        int n_groups, uint8_t* mask, int32_t* kv_count,
+                        int32_t* kv_index, int64_t* head_load, float* head_density,
+                        int64_t* added, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
  * Block-sparse attention over the kept blocks.
  *
  * Source: only the (query block, key block) pairs the routing keeps are
@@ -246,6 +333,9 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
  *   output is the same bits as without claims.  Honoured by the q-block-pair
  *   kernel (group 2, FVATTN_V_TILES, an MFMA shape); the other kernels run
  *   their lists as given.
+ * claim_groups (0 <= x <= 64): 0 or 1 lets a workgroup claim from every
+ *   list; x > 1 only from the lists w' with w' % x == w % x, so the worker
+ *   groups of fvattn_schedule_heads stay independent, like ranks.
  * out_rows (nullable, device int32 [n]): result row r of every head is stored
  *   at row out_rows[r] of o instead of row r; passing the Hilbert order `perm`
  *   of fvattn_hilbert_permute writes O straight back in token order, which
@@ -262,8 +352,8 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o,
                        const int32_t* kv_count,
                        const int32_t* kv_index, const int32_t* worker_offsets,
                        const int32_t* worker_tiles, int n_workers,
-                       uint64_t* timing, int32_t* claims, const int32_t* out_rows,
-                       hipStream_t stream);
+                       uint64_t* timing, int32_t* claims, int claim_groups,
+                       const int32_t* out_rows, hipStream_t stream);
 
 /*
  * Persistent workers for fvattn_sparse_attn on the current device: the

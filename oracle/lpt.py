@@ -31,6 +31,8 @@ X groups of workers (worker w is in group w % X) by the same LPT rule on
 head loads, then every tile goes, in the global LPT order, to the
 least-loaded worker of its head's group.  Pins: X = 1 gives lpt_schedule
 exactly; tiles stay in their head's group; conservation; a hand example.
+The head -> group map can also be given (the per-rank image of SASA/RLB,
+oracle/sasa.py); the pins then check that tiles stay in the given groups.
 """
 from __future__ import annotations
 
@@ -98,17 +100,21 @@ def head_groups(head_loads: np.ndarray, groups: int) -> np.ndarray:
     return out
 
 
-def lpt_schedule_grouped(costs_2d, n_workers: int, groups: int, tile_order: bool = False):
+def lpt_schedule_grouped(costs_2d, n_workers: int, groups: int, tile_order: bool = False,
+                         head_group=None):
     """Two-level LPT.  costs_2d [H, tiles per head]; worker w belongs to group
     w % X with X = min(groups, n_workers).  Heads go to groups by LPT on their
-    summed tile costs; then each tile, in the global (cost desc, id asc)
-    order, goes to the least-loaded worker of its head's group (lowest index
-    on ties).  Returns (order, worker_offsets, worker_tiles, worker_load)
-    like lpt_schedule."""
+    summed tile costs (or as `head_group` gives them); then each tile, in the
+    global (cost desc, id asc) order, goes to the least-loaded worker of its
+    head's group (lowest index on ties).  Returns (order, worker_offsets,
+    worker_tiles, worker_load) like lpt_schedule."""
     c2 = np.asarray(costs_2d, dtype=np.int64)
     H, tph = c2.shape
     X = max(1, min(int(groups), n_workers))
-    hg = head_groups(c2.sum(axis=1), X)
+    if head_group is None:
+        hg = head_groups(c2.sum(axis=1), X)
+    else:
+        hg = np.clip(np.asarray(head_group, dtype=np.int64), 0, X - 1)
     costs = c2.reshape(-1)
     order = lpt_order(costs)
     loads = np.zeros(n_workers, dtype=np.int64)

@@ -24,7 +24,7 @@ def test_library_is_built_in_tree():
 def test_exports_every_declared_symbol():
     lib = _lib.load_library()
     declared = _lib.declared_symbols()
-    assert len(declared) == 11, declared
+    assert len(declared) == 15, declared
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
@@ -55,6 +55,12 @@ def test_workspace_sizes():
     assert lib.fvattn_schedule_workspace_size(40, 591, 256) == (
         10 * rnd(40 * 591 * 4) + rnd((2048 + 65) * 4))
     assert lib.fvattn_schedule_workspace_size(40, 591, 0) == 0
+    # SASA: row stats (float2) + 256-bin histograms + group state (16 B) +
+    # per-row tie counts (int32) and offsets (int64)
+    rows = 40 * 591
+    assert lib.fvattn_sasa_workspace_size(40, 75600, 128, 8) == (
+        rnd(8 * rows) + rnd(4 * 256 * 8) + rnd(16 * 8) + rnd(4 * rows) + rnd(8 * rows))
+    assert lib.fvattn_sasa_workspace_size(40, 75600, 128, 0) == 0
 
 
 def _validation_main():
@@ -95,22 +101,22 @@ def _validation_main():
         (lib.fvattn_schedule(P, 40, 591, 1, 4, 8 << 8, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule(P, 4097, 2, 1, 256, 8 << 8, P, P, P, P, P, 1 << 30, N), EUNS),
         # attention
-        (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 256, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, N, N), EUNS),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, float("inf"), P, P, N, N, 0, N, N, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, N, 4, N, N, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, P, 0, N, N, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, P, N, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 256, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EUNS),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, float("inf"), P, P, N, N, 0, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, N, 4, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, P, 0, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, P, N, 0, N, N), EINVAL),
         # run-time claims need the persistent launch
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, P, N, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 2, 1, 0.0, P, P, N, N, 0, N, N, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, P, 0, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 2, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         # workers
         (lib.fvattn_attn_workers(1, 128, 128, 1, 2, N), EINVAL),
         (lib.fvattn_attn_workers(1, 128, 128, 1, 3, ctypes.byref(ctypes.c_int())), EINVAL),
         (lib.fvattn_attn_workers(1, 128, 128, 5, 1, ctypes.byref(ctypes.c_int())), EINVAL),
         (lib.fvattn_schedule(P, 40, 591, 3, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 1, 3, 0.0, P, P, N, N, 0, N, N, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 1, 3, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         # pack_v
         (lib.fvattn_pack_v(P, P, P, 1, 128, 64, 16, 1, N), EINVAL),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 16, 0, N), EUNS),
@@ -119,8 +125,41 @@ def _validation_main():
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 12, 1, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 8, 1, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 24, 1, N), EUNS),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 12, 1, 1, 0.0, P, P, N, N, 0, N, N, N, N), EUNS),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 12, 1, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EUNS),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), N, 1, 128, 64, 16, 1, N), EINVAL),
+        # claim groups: 0..64
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, P, 4, N, P, 65, N, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, P, 4, N, P, -1, N, N), EINVAL),
+        # schedule with given head groups
+        (lib.fvattn_schedule_heads(P, 40, 591, 1, 256, 8, N, 0, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule_heads(P, 40, 591, 1, 256, 1, P, 0, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule_heads(P, 40, 591, 1, 256, 65, P, 0, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule_heads(P, 40, 591, 1, 4, 8, P, 0, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule_heads(P, 40, 591, 1, 256, 8, P, 8 << 8, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule_heads(P, 40, 591, 3, 256, 8, P, 0, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule_heads(P, 40, 591, 1, 2049, 8, P, 0, P, P, P, P, P, 1 << 30, N), EUNS),
+        (lib.fvattn_schedule_heads(P, 40, 591, 1, 256, 8, P, 0, P, P, P, P, P, 100, N), EWS),
+        # SASA plan: thresholds and sizes
+        (lib.fvattn_sasa_plan(N, 40, 8, 1.05, 1.10, 0.8, 0.07, P, P, P, N), EINVAL),
+        (lib.fvattn_sasa_plan(P, 0, 8, 1.05, 1.10, 0.8, 0.07, P, P, P, N), EINVAL),
+        (lib.fvattn_sasa_plan(P, 40, 0, 1.05, 1.10, 0.8, 0.07, P, P, P, N), EINVAL),
+        (lib.fvattn_sasa_plan(P, 40, 8, 0.95, 1.10, 0.8, 0.07, P, P, P, N), EINVAL),
+        (lib.fvattn_sasa_plan(P, 40, 8, 1.05, 1.00, 0.8, 0.07, P, P, P, N), EINVAL),
+        (lib.fvattn_sasa_plan(P, 40, 8, 1.05, float("inf"), 0.8, 0.07, P, P, P, N), EINVAL),
+        (lib.fvattn_sasa_plan(P, 40, 8, 1.05, 1.10, 1.5, 0.07, P, P, P, N), EINVAL),
+        (lib.fvattn_sasa_plan(P, 40, 8, 1.05, 1.10, 0.8, -0.1, P, P, P, N), EINVAL),
+        (lib.fvattn_sasa_plan(P, 40, 8, 1.05, 1.10, float("nan"), 0.07, P, P, P, N), EINVAL),
+        (lib.fvattn_sasa_plan(P, 4097, 8, 1.05, 1.10, 0.8, 0.07, P, P, P, N), EUNS),
+        (lib.fvattn_sasa_plan(P, 40, 65, 1.05, 1.10, 0.8, 0.07, P, P, P, N), EUNS),
+        # SASA augment
+        (lib.fvattn_sasa_augment(N, 1 << 30, 1, 128, 64, 16, P, P, 2, P, P, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_sasa_augment(P, 1 << 30, 1, 128, 64, 16, P, P, 0, P, P, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_sasa_augment(P, 1 << 30, 1, 128, 64, 16, P, P, 2, P, P, P, P, P, N, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_sasa_augment(P, 1 << 30, 1, 4097 * 16, 64, 16, P, P, 2, P, P, P, P, P, P, P, 1 << 30, N), EUNS),
+        (lib.fvattn_sasa_augment(P, 1 << 30, 1, 128, 64, 16, P, P, 65, P, P, P, P, P, P, P, 1 << 30, N), EUNS),
+        (lib.fvattn_sasa_augment(P, 16, 1, 128, 64, 16, P, P, 2, P, P, P, P, P, P, P, 1 << 30, N), EWS),
+        (lib.fvattn_sasa_augment(P, 1 << 30, 1, 128, 64, 16, P, P, 2, P, P, P, P, P, P, N, 1 << 30, N), EWS),
+        (lib.fvattn_sasa_augment(P, 1 << 30, 1, 128, 64, 16, P, P, 2, P, P, P, P, P, P, P, 8, N), EWS),
     ]
     bad = [(i, got, want) for i, (got, want) in enumerate(checks) if got != want]
     if bad:

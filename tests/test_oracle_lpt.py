@@ -154,3 +154,30 @@ def test_grouped_tiles_stay_in_their_group(seed):
         if tl.size:
             c = costs.reshape(-1)[tl]
             assert loads[ws].max() <= c.sum() / ws.size + c.max() + 1e-9
+
+
+def test_grouped_given_head_groups_hand_example():
+    # 2 groups, workers 0, 2 (group 0) and 1, 3 (group 1); all three heads
+    # forced into group 1 by the given map, so group 0's workers stay empty
+    costs = np.array([[5, 1], [4, 2], [3, 3]])
+    order, offs, tiles, loads = lpt.lpt_schedule_grouped(costs, 4, 2, head_group=[1, 1, 1])
+    # LPT order: t0 (5), t2 (4), t4 (3), t5 (3), t3 (2), t1 (1); each to the
+    # less-loaded of workers 1 and 3
+    assert order.tolist() == [0, 2, 4, 5, 3, 1]
+    assert loads.tolist() == [0, 9, 0, 9]
+    assert offs.tolist() == [0, 0, 3, 3, 6]
+    assert tiles.tolist() == [0, 5, 1, 2, 4, 3]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_grouped_given_groups_tiles_stay_in_them(seed):
+    rng = np.random.default_rng(seed)
+    H, tph, W, X = 7, 5, 12, 4
+    costs = rng.integers(0, 20, size=(H, tph))
+    hg = rng.integers(0, X, size=H)
+    _, offs, tiles, loads = lpt.lpt_schedule_grouped(costs, W, X, head_group=hg)
+    for w in range(W):
+        for t in tiles[offs[w]:offs[w + 1]]:
+            assert hg[t // tph] == w % X
+    assert sorted(tiles.tolist()) == list(range(H * tph))
+    assert loads.sum() == costs.sum()

@@ -10,7 +10,6 @@ import pytest
 from oracle import sasa
 
 
-
 def test_static_groups_contiguous():
     assert sasa.static_groups(40, 8).tolist() == sum([[g] * 5 for g in range(8)], [])
     # fewer heads than groups: some groups stay empty
