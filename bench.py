@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from block_sparse_attention_11_amd import synth  # noqa: E402
-from block_sparse_attention_11_amd.pipeline import FVAttnPath  # noqa: E402
+from block_sparse_attention_11_amd.pipeline import XCDS, FVAttnPath  # noqa: E402
 
 METRIC = "effective TFLOP/s on kept blocks + speedup vs dense, 720p-shaped, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0           # MI355X dense bf16 MFMA
@@ -139,6 +139,8 @@ def timed_step(path, q, k, v, out, p, kf, tm: StageTimer | None, balanced=True,
     path.to_hilbert(q, k, v)
     if tm: tm.mark("s2")
     path.route(p, kf)
+    if path.ranks > 1:
+        path.plan_ranks()          # per-rank image: head moves (+ SASA blocks)
     if tm: tm.mark("s3")
     path.schedule()
     if tm: tm.mark("s4")
@@ -162,6 +164,75 @@ def run_steps(path, q, k, v, out, p, kf, steps, warmup, balanced=True, runtime=T
               for i, nm in enumerate(names)}
     step_ms = float(np.mean(tm.durations("s0", "s5")))
     return wall * 1e3, step_ms, stages
+
+
+def rel_l2(a, b) -> float:
+    """||a - b|| / ||b|| over [H, n, d] tensors, one head at a time in fp32."""
+    num = den = 0.0
+    for h in range(a.shape[0]):
+        x, y = a[h].float(), b[h].float()
+        num += float(((x - y) ** 2).sum())
+        den += float((y ** 2).sum())
+    return (num / max(den, 1e-300)) ** 0.5
+
+
+def group_end_ms(timing: np.ndarray, groups: int):
+    """Per worker group (w % groups): its last workgroup end after the first
+    start of the launch, in ms (100 MHz stamps)."""
+    t = timing.astype(np.uint64)
+    start = t[:, 0].astype(np.float64)
+    end = t[:, 1].astype(np.float64)
+    t0 = start.min()
+    ends = np.array([end[g::groups].max() - t0 for g in range(groups)]) / 1e5
+    return ends
+
+
+def sasa_report(w, q, k, v, steps: int, warmup: int, dense_out=None, default_out=None):
+    """The per-rank image on 8 XCD worker groups, with and without SASA:
+    quality (relative L2 to the dense p = 1 output) at the makespan of the
+    groups, which work independently like ranks."""
+    G = XCDS
+    if dense_out is None:
+        pd = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, device="cuda")
+        dense_out = torch.empty_like(q)
+        pd.run(q, k, v, 1.0, 0, out=dense_out)
+        del pd
+    rep = {"groups": G, "workload": w.name}
+    if default_out is not None:
+        rep["default_path_rel_l2_vs_dense"] = rel_l2(default_out, dense_out)
+    for name, aug in (("no_sasa", False), ("sasa", True)):
+        log(f"per-rank image, {name}")
+        path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, device="cuda",
+                          ranks=G, sasa=aug)
+        o = torch.empty_like(q)
+        _, step_ms, stages = run_steps(path, q, k, v, o, w.p, w.k, steps, warmup)
+        info = path.sasa_info.cpu().numpy()
+        ends = group_end_ms(path.timing.cpu().numpy(), G)
+        dens = path.head_density.cpu().numpy()
+        r = {"attention_ms": round(stages["attention"], 4),
+             "step_ms": round(step_ms, 4),
+             "route_and_plan_ms": round(stages["route"], 4),
+             "kept_tflop": round(kept_flops(path) / 1e12, 4),
+             "density_mean": round(float(dens.mean()), 5),
+             "group_end_ms": [round(float(x), 3) for x in ends],
+             "group_end_max_over_mean": round(float(ends.max() / ends.mean()), 4),
+             "rel_l2_vs_dense": rel_l2(o, dense_out)}
+        if name == "no_sasa":
+            lb, la = info[2:2 + G], info[2 + G:]
+            rep["plan"] = {"mode": int(info[0]), "moves": int(info[1]),
+                           "group_loads_before": lb.tolist(), "group_loads_after": la.tolist(),
+                           "rho_before": round(float(lb.max() / lb.mean()), 4),
+                           "rho_after": round(float(la.max() / la.mean()), 4),
+                           "budget": path.group_budget.cpu().numpy().tolist()}
+        else:
+            r["added_blocks"] = path.sasa_added.cpu().numpy().tolist()
+        rep[name] = r
+        del path, o
+    rep["sasa_makespan_ratio"] = round(rep["sasa"]["attention_ms"] /
+                                       rep["no_sasa"]["attention_ms"], 4)
+    rep["sasa_rel_l2_ratio"] = round(rep["sasa"]["rel_l2_vs_dense"] /
+                                     max(rep["no_sasa"]["rel_l2_vs_dense"], 1e-300), 4)
+    return rep
 
 
 def cpu_baseline(q, k, v, w, budget_s=15.0, max_tiles=400):
@@ -223,6 +294,9 @@ def main():
     ap.add_argument("--no-controls", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--sasa", action="store_true",
+                    help="also report the per-rank image on the 8 XCD groups with and "
+                         "without slack-aware sparse augmentation")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the multi-GPU head-migration path is "
@@ -313,6 +387,10 @@ def main():
                       "pages_dit_speedup_8xH20": "2.02-2.11",
                       "pages_imbalance_before_after_rlb_8xH20": "1.34 -> 1.08",
                       "pages_attention_share_of_generation_1xH20": 0.741}
+    if args.sasa:
+        res["sasa"] = sasa_report(w, q, k, v, max(2, args.dense_steps), 1,
+                                  dense_out=None if args.no_controls else o2,
+                                  default_out=out)
     if not args.no_cpu_baseline:
         log("cpu oracle baseline")
         res["cpu_baseline"] = cpu_baseline(q, k, v, w)
