@@ -763,7 +763,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
 // in-flight copy): the copy of union block u+1 is issued right after the one
 // barrier of block u and overlaps all of block u's work.
 // ---------------------------------------------------------------------------
-template <int D, int BLK, bool PERSIST>
+template <int D, int BLK, bool PERSIST, bool CONFINED = false>
 __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 2 * BLK / 32;            // wavefronts, both q-blocks
@@ -888,11 +888,20 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
       if (pos < 0) {
         // the list with the most unclaimed tiles (ties: lowest index)
         int best_rem = 0, best_v = -1;
-        for (int base = 0; base < W; base += 64) {
-          const int v = base + lane;
+        // candidates: every list, or (the CONFINED instance, claim_groups =
+        // x > 1) the lists of this group only, v = own % x + x * k; a
+        // separate instance keeps the group arithmetic out of the default
+        // kernel's registers
+        int gx = 1, g0 = 0, span = W;
+        if constexpr (CONFINED) {
+          gx = a.claim_groups;
+          g0 = own % gx;
+          span = (W - g0 + gx - 1) / gx;
+        }
+        for (int base = 0; base < span; base += 64) {
+          const int v = g0 + gx * (base + lane);
           int rem = 0;
-          const int X = a.claim_groups;
-          if (v < W && v != own && (X <= 1 || v % X == own % X)) {
+          if (base + lane < span && v != own) {
             const int lo = a.worker_offsets[v], hi = a.worker_offsets[v + 1];
             rem = hi - lo - __hip_atomic_load(a.claims + v, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
@@ -1180,7 +1189,10 @@ hipError_t launch_mfma_pair(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(claims_reset_kernel, dim3((a.n_workers + 255) / 256), dim3(256), 0, s,
                        a.claims, a.n_workers);
   }
-  if (a.worker_offsets) {
+  if (a.worker_offsets && a.claims && a.claim_groups > 1) {
+    hipLaunchKernelGGL((attn_mfma_pair_kernel<D, BLK, true, true>), dim3(a.n_workers),
+                       dim3(4 * BLK), 0, s, a);
+  } else if (a.worker_offsets) {
     hipLaunchKernelGGL((attn_mfma_pair_kernel<D, BLK, true>), dim3(a.n_workers),
                        dim3(4 * BLK), 0, s, a);
   } else {
