@@ -348,10 +348,21 @@ def main():
                         "density_min": round(float(dens.min()), 5),
                         "density_max": round(float(dens.max()), 5)}
     res["stages_ms"] = {k2: round(v2, 4) for k2, v2 in stages.items()}
-    route_bytes = (2 * w.heads * w.n * w.d * 2 + w.heads * path.nb ** 2
-                   + 4 * int(path.head_load.sum().item()) + 4 * w.heads * path.nb)
-    res["route"] = {"ms": round(stages["route"], 4), "algorithmic_bytes": route_bytes,
-                    "gbs": round(route_bytes / (stages["route"] * 1e-3) / 1e9, 1)}
+    esz = 2 if dt == torch.bfloat16 else 4
+    lists = w.heads * path.nb ** 2 + 4 * int(path.head_load.sum().item()) + 4 * w.heads * path.nb
+    qk = 2 * w.heads * w.n * w.d * esz
+    if path.fused:
+        # pooling rides in the Q/K gather: the front end reads Q, K once and
+        # writes their Hilbert copies, the mask and the kept lists
+        front_ms = stages["permute_in"] + stages["route"]
+        res["route"] = {"ms": round(stages["route"], 4), "pooling": "fused into the Q/K gather",
+                        "front_end_ms": round(front_ms, 4),
+                        "front_end_algorithmic_bytes": 2 * qk + lists,
+                        "front_end_gbs": round((2 * qk + lists) / (front_ms * 1e-3) / 1e9, 1)}
+    else:
+        route_bytes = qk + lists
+        res["route"] = {"ms": round(stages["route"], 4), "algorithmic_bytes": route_bytes,
+                        "gbs": round(route_bytes / (stages["route"] * 1e-3) / 1e9, 1)}
     res["imbalance"] = dict(imb, predicted_lpt_max_over_mean=float(wl.max() / wl.mean()))
     traffic = read_traffic(w.name)
     res["roofline"] = {"bound": "mfma", "achieved": round(attn_tflops, 2),
@@ -368,6 +379,11 @@ def main():
         _, _, st_static = run_steps(path, q, k, v, o2, w.p, w.k, max(2, args.dense_steps), 1,
                                     runtime=False)
         imb_static = cu_imbalance(path.timing.cpu().numpy())
+        log("one-stream unfused control")
+        p1 = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=dt, n_workers=path.n_workers,
+                        device="cuda", group=args.group or None, fused=False, overlap=False)
+        _, step1_ms, st1 = run_steps(p1, q, k, v, o2, w.p, w.k, max(2, args.dense_steps), 1)
+        del p1
         log("dense p=1 control")
         _, _, st_dense = run_steps(path, q, k, v, o2, 1.0, 0, args.dense_steps, 1)
         dense_flops = kept_flops(path)
@@ -380,6 +396,10 @@ def main():
             "dense_attention_ms": round(st_dense["attention"], 4),
             "dense_tflops": round(dense_flops / (st_dense["attention"] * 1e-3) / 1e12, 2),
             "speedup_vs_dense_attention": round(st_dense["attention"] / attn_ms, 4),
+            "one_stream_unfused_step_ms": round(step1_ms, 4),
+            "one_stream_unfused_stages_ms": {k2: round(v2, 4) for k2, v2 in st1.items()},
+            "step_ms": round(step_ms, 4),
+            "fusion_overlap_saving_ms": round(step1_ms - step_ms, 4),
             "path_speedup_vs_dense_attention": round(
                 st_dense["attention"] / (stages["route"] + stages["schedule"] + attn_ms), 4),
         }

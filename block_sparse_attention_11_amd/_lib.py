@@ -49,6 +49,11 @@ _SIGNATURES = {
                               _c_int, _c_float, _c_int, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                               _c_void_p]),
+    "fvattn_permute_pool": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                     _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
+    "fvattn_route_pooled": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                     _c_float, _c_int, _c_void_p, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "fvattn_schedule_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int]),
     "fvattn_schedule": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_void_p,
@@ -198,6 +203,44 @@ def route(q, k, block: int, p: float, k_floor: int, mask, kv_count, kv_index,
         _ptr(q), _ptr(k), _dtype_code(q), H, n, d, block, float(p), int(k_floor),
         _ptr(mask), _ptr(kv_count), _ptr(kv_index), _ptr(head_load),
         _ptr(head_density), _ptr(workspace), ws_bytes, _stream(q)))
+
+
+def permute_pool(src: torch.Tensor, dst: torch.Tensor, index: torch.Tensor, block: int,
+                 pooled: torch.Tensor):
+    """dst <- rows of src gathered by index, and pooled [heads, nB, d] fp32 <-
+    the column means of each block of dst rows, in one pass."""
+    _dev(src, dst, index, pooled)
+    _need(src.dim() == 3 and src.shape == dst.shape and src.dtype == dst.dtype,
+          "src/dst must be [heads, n, d] of one dtype")
+    H, n, d = src.shape
+    nb = (n + block - 1) // block
+    _need(index.dtype == torch.int32 and index.numel() == n, "index int32[n]")
+    _need(pooled.dtype == torch.float32 and pooled.numel() == H * nb * d,
+          "pooled f32[heads, nB, d]")
+    _check("fvattn_permute_pool", load_library().fvattn_permute_pool(
+        _ptr(src), _ptr(dst), _ptr(index), H, n, d, block, _dtype_code(src), _ptr(pooled),
+        _stream(src)))
+
+
+def route_pooled(qbar, kbar, n: int, block: int, p: float, k_floor: int, mask, kv_count,
+                 kv_index, head_load, head_density, workspace):
+    """route() from pooled means qbar, kbar [heads, nB, d] fp32 of n-row tensors."""
+    _dev(qbar, kbar, mask, kv_count, kv_index, head_load, head_density, workspace)
+    _need(qbar.shape == kbar.shape and qbar.dim() == 3 and qbar.dtype == torch.float32
+          and kbar.dtype == torch.float32, "qbar, kbar f32[H, nB, d]")
+    H, nb, d = qbar.shape
+    _need(nb == (n + block - 1) // block, "qbar rows must be ceil(n / block)")
+    _need(mask.dtype == torch.uint8 and mask.numel() == H * nb * nb, "mask u8[H,nB,nB]")
+    _need(kv_count.dtype == torch.int32 and kv_count.numel() == H * nb, "kv_count")
+    _need(kv_index.dtype == torch.int32 and kv_index.numel() == H * nb * nb, "kv_index")
+    _need(head_load.dtype == torch.int64 and head_load.numel() == H, "head_load")
+    _need(head_density.dtype == torch.float32 and head_density.numel() == H,
+          "head_density")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("fvattn_route_pooled", load_library().fvattn_route_pooled(
+        _ptr(qbar), _ptr(kbar), H, n, d, block, float(p), int(k_floor),
+        _ptr(mask), _ptr(kv_count), _ptr(kv_index), _ptr(head_load),
+        _ptr(head_density), _ptr(workspace), ws_bytes, _stream(qbar)))
 
 
 def schedule_workspace_size(heads: int, n_qblocks: int, n_workers: int) -> int:

@@ -93,6 +93,38 @@ int fvattn_route(const void* q, const void* k, int dtype, int heads, int n, int 
                                             head_load, head_density, ws, stream));
 }
 
+int fvattn_permute_pool(const void* src, void* dst, const int32_t* index, int heads, int n,
+                        int d, int block, int dtype, float* pooled, hipStream_t stream) {
+  if (!src || !dst || !index || !pooled) return FVATTN_EINVAL;
+  if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
+  if (src == dst) return FVATTN_EINVAL;
+  if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
+  if (((uintptr_t)src | (uintptr_t)dst) % 16 != 0) return FVATTN_EINVAL;
+  if (d > 256 || (dtype == FVATTN_BF16 ? d % 8 : d % 4) != 0) return FVATTN_EUNSUPPORTED;
+  return launch_status(fvattn::launch_permute_pool(src, dst, index, dtype == FVATTN_BF16, heads,
+                                                   n, d, block, pooled, stream));
+}
+
+int fvattn_route_pooled(const float* qbar, const float* kbar, int heads, int n, int d,
+                        int block, float p, int k_floor, uint8_t* mask, int32_t* kv_count,
+                        int32_t* kv_index, int64_t* head_load, float* head_density,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!qbar || !kbar || !mask || !kv_count || !kv_index || !head_load || !head_density)
+    return FVATTN_EINVAL;
+  if (heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
+  if (!(p > 0.f) || isnan(p) || k_floor < 0) return FVATTN_EINVAL;
+  if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
+  const int64_t nb = nblocks(n, block);
+  if (d > 256 || d % 4 != 0) return FVATTN_EUNSUPPORTED;
+  if (nb > 4096) return FVATTN_EUNSUPPORTED;
+  const size_t need = fvattn::route_workspace_bytes(heads, n, d, block);
+  if (!workspace || workspace_bytes < need) return FVATTN_EWORKSPACE;
+  const fvattn::RouteWorkspace ws = fvattn::route_carve(workspace, heads, n, d, block);
+  return launch_status(fvattn::launch_route_pooled(qbar, kbar, heads, n, d, block, p, k_floor,
+                                                   mask, kv_count, kv_index, head_load,
+                                                   head_density, ws, stream));
+}
+
 size_t fvattn_schedule_workspace_size(int heads, int n_qblocks, int n_workers) {
   if (heads < 1 || n_qblocks < 1 || n_workers < 1) return 0;
   return fvattn::schedule_workspace_bytes(heads, n_qblocks, n_workers);

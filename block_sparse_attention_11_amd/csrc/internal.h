@@ -48,6 +48,18 @@ hipError_t launch_route(const void* q, const void* k, bool bf16, int heads,
                         uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
                         int64_t* head_load, float* head_density,
                         const RouteWorkspace& ws, hipStream_t s);
+// routing from given pooled means (qbar, kbar [heads][nB][d] fp32); writes
+// the scores into ws.z and leaves ws.qbar / ws.kbar alone
+hipError_t launch_route_pooled(const float* qbar, const float* kbar, int heads, int n,
+                               int d, int block, float p, int k_floor, uint8_t* mask,
+                               int32_t* kv_count, int32_t* kv_index, int64_t* head_load,
+                               float* head_density, const RouteWorkspace& ws,
+                               hipStream_t s);
+// dst[h][r] = src[h][index[r]] and pooled[h][j] = the column means of the
+// gathered rows of block j, one pass
+hipError_t launch_permute_pool(const void* src, void* dst, const int32_t* index, bool bf16,
+                               int heads, int n, int d, int block, float* pooled,
+                               hipStream_t s);
 // per-head sum of kv_count (int64) and density = sum / nB^2
 hipError_t launch_head_load(const int32_t* kv_count, int heads, int nb, int64_t* head_load,
                             float* head_density, hipStream_t s);

@@ -33,13 +33,13 @@ constexpr int kSelectThreads = 256;
 constexpr int kScoreTile = 64;
 constexpr int kScoreK = 16;
 
-__device__ inline void load_vec(const float* p, float out[4]) {
-  const float4 v = *reinterpret_cast<const float4*>(p);
-  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+// One 16-byte vector of a row as fp32 values (bf16 widened exactly).
+__device__ inline void unpack_vec(const uint4& v, float out[4], const float*) {
+  out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
 }
 
-__device__ inline void load_vec(const bf16s* p, float out[8]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
+__device__ inline void unpack_vec(const uint4& v, float out[8], const bf16s*) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -51,18 +51,19 @@ __device__ inline void load_vec(const bf16s* p, float out[8]) {
 template <typename T>
 struct VecWidth { static constexpr int value = 16 / sizeof(T); };
 
-// blockIdx.x = key/query block j, blockIdx.y = head, blockIdx.z = 0 (Q) / 1 (K)
-template <typename T>
-__global__ __launch_bounds__(kPoolThreads) void pool_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ qbar,
-    float* __restrict__ kbar, int n, int d, int block, int nb) {
+constexpr int kPoolBatch = 8;   // rows one thread has in flight
+
+// Column means of rows r0..r1-1 of one block, in one fixed fp32 order:
+// thread (rsub, lane) adds rows r0 + rsub + t * rows_per_pass in ascending t,
+// then the rsub partials are added in ascending rsub.  Row r is read from
+// src row (GATHER ? index[r] : r); with GATHER it is also stored to out row
+// r, so the gather into Hilbert order and the pooling read the rows once.
+template <typename T, bool GATHER>
+__device__ inline void pool_block(const T* __restrict__ src, T* __restrict__ out,
+                                  const int32_t* __restrict__ index,
+                                  float* __restrict__ mean, int r0, int r1, int d,
+                                  float* red) {
   constexpr int VE = VecWidth<T>::value;
-  __shared__ float red[kPoolThreads * VE];
-  const int j = blockIdx.x, h = blockIdx.y;
-  const T* src = (blockIdx.z == 0 ? q : k) + (size_t)h * n * d;
-  float* dst = (blockIdx.z == 0 ? qbar : kbar) + ((size_t)h * nb + j) * d;
-  const int r0 = j * block;
-  const int r1 = min(n, r0 + block);
   const int lanes_per_row = d / VE;
   const int rows_per_pass = kPoolThreads / lanes_per_row;
   const int tid = threadIdx.x;
@@ -72,11 +73,28 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
 #pragma unroll
   for (int e = 0; e < VE; ++e) acc[e] = 0.f;
   if (rsub < rows_per_pass) {
-    for (int r = r0 + rsub; r < r1; r += rows_per_pass) {
-      float x[VE];
-      load_vec(src + (size_t)r * d + lane * VE, x);
+    for (int rb = r0 + rsub; rb < r1; rb += kPoolBatch * rows_per_pass) {
+      uint4 raw[kPoolBatch];
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc[e] += x[e];
+      for (int t = 0; t < kPoolBatch; ++t) {
+        const int r = rb + t * rows_per_pass;
+        if (r < r1) {
+          const size_t sr = GATHER ? (size_t)index[r] : (size_t)r;
+          raw[t] = *reinterpret_cast<const uint4*>(src + sr * d + lane * VE);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kPoolBatch; ++t) {
+        const int r = rb + t * rows_per_pass;
+        if (r < r1) {
+          if constexpr (GATHER)
+            *reinterpret_cast<uint4*>(out + (size_t)r * d + lane * VE) = raw[t];
+          float x[VE];
+          unpack_vec(raw[t], x, src);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[e] += x[e];
+        }
+      }
     }
   }
 #pragma unroll
@@ -88,8 +106,37 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
   for (int col = tid; col < d; col += kPoolThreads) {
     float s = 0.f;
     for (int rs = 0; rs < used; ++rs) s += red[rs * d + col];
-    dst[col] = s * inv;
+    mean[col] = s * inv;
   }
+}
+
+// blockIdx.x = key/query block j, blockIdx.y = head, blockIdx.z = 0 (Q) / 1 (K)
+template <typename T>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ qbar,
+    float* __restrict__ kbar, int n, int d, int block, int nb) {
+  __shared__ float red[kPoolThreads * VecWidth<T>::value];
+  const int j = blockIdx.x, h = blockIdx.y;
+  const T* src = (blockIdx.z == 0 ? q : k) + (size_t)h * n * d;
+  float* dst = (blockIdx.z == 0 ? qbar : kbar) + ((size_t)h * nb + j) * d;
+  const int r0 = j * block;
+  pool_block<T, false>(src, nullptr, nullptr, dst, r0, min(n, r0 + block), d, red);
+}
+
+// Gather into Hilbert order fused with the pooling: blockIdx.x = block j,
+// blockIdx.y = head; out[h][r] = src[h][index[r]] for the rows of block j
+// and pooled[h][j] = their column means (the same values pool_kernel gives
+// for the gathered tensor, bit for bit).
+template <typename T>
+__global__ __launch_bounds__(kPoolThreads) void permute_pool_kernel(
+    const T* __restrict__ src, T* __restrict__ out, const int32_t* __restrict__ index,
+    float* __restrict__ pooled, int n, int d, int block, int nb) {
+  __shared__ float red[kPoolThreads * VecWidth<T>::value];
+  const int j = blockIdx.x, h = blockIdx.y;
+  const size_t head = (size_t)h * n * d;
+  const int r0 = j * block;
+  pool_block<T, true>(src + head, out + head, index, pooled + ((size_t)h * nb + j) * d, r0,
+                      min(n, r0 + block), d, red);
 }
 
 // z[h][i][j] = scale * sum_c qbar[h][i][c] * kbar[h][j][c]
@@ -305,6 +352,20 @@ hipError_t launch_head_load(const int32_t* kv_count, int heads, int nb, int64_t*
   return hipGetLastError();
 }
 
+hipError_t launch_permute_pool(const void* src, void* dst, const int32_t* index, bool bf16,
+                               int heads, int n, int d, int block, float* pooled,
+                               hipStream_t s) {
+  const int nb = (n + block - 1) / block;
+  if (bf16) {
+    hipLaunchKernelGGL(permute_pool_kernel<bf16s>, dim3(nb, heads), dim3(kPoolThreads), 0, s,
+                       (const bf16s*)src, (bf16s*)dst, index, pooled, n, d, block, nb);
+  } else {
+    hipLaunchKernelGGL(permute_pool_kernel<float>, dim3(nb, heads), dim3(kPoolThreads), 0, s,
+                       (const float*)src, (float*)dst, index, pooled, n, d, block, nb);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const void* q, const void* k, bool bf16, int heads,
                         int n, int d, int block, float p, int k_floor,
                         uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
@@ -322,10 +383,20 @@ hipError_t launch_route(const void* q, const void* k, bool bf16, int heads,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_route_pooled(ws.qbar, ws.kbar, heads, n, d, block, p, k_floor, mask,
+                             kv_count, kv_index, head_load, head_density, ws, s);
+}
+
+hipError_t launch_route_pooled(const float* qbar, const float* kbar, int heads, int n,
+                               int d, int block, float p, int k_floor, uint8_t* mask,
+                               int32_t* kv_count, int32_t* kv_index, int64_t* head_load,
+                               float* head_density, const RouteWorkspace& ws,
+                               hipStream_t s) {
+  const int nb = (n + block - 1) / block;
   const unsigned tiles = (unsigned)((nb + kScoreTile - 1) / kScoreTile);
   hipLaunchKernelGGL(score_kernel, dim3(tiles, tiles, heads), dim3(256), 0, s,
-                     ws.qbar, ws.kbar, ws.z, nb, d, 1.0f / sqrtf((float)d));
-  e = hipGetLastError();
+                     qbar, kbar, ws.z, nb, d, 1.0f / sqrtf((float)d));
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int np = 1;
   while (np < nb) np <<= 1;

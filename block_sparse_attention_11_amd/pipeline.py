@@ -4,9 +4,12 @@ Allocation and call order only; each step is one C-ABI call into the HIP
 library:
 
     hilbert_permute  (once per grid shape)
-    permute_rows     Q, K -> Hilbert order
-    pack_v           V -> Hilbert order, one transposed tile per key block
-    route            pooled-Q/K Top-p + Top-k -> mask, kept lists, head load
+    permute_pool     Q, K -> Hilbert order, with the pooled block means in the
+                     same pass (fused=False: permute_rows, pooling in route)
+    pack_v           V -> Hilbert order, one transposed tile per key block; with
+                     overlap=True on a second stream, concurrent with routing
+                     and scheduling (V feeds neither), joined before attention
+    route_pooled     pooled-Q/K Top-p + Top-k -> mask, kept lists, head load
     [sasa_plan, sasa_augment   per-rank image only: head moves and extra
                      blocks on the groups off the critical path]
     schedule         LPT work list over (head, q-block) tiles
@@ -41,7 +44,8 @@ class FVAttnPath:
     def __init__(self, heads: int, grid, d: int, block: int, dtype=torch.bfloat16,
                  n_workers: int | None = None, device="cuda", tile_order: bool = False,
                  v_tiles: bool | None = None, group: int | None = None,
-                 worker_groups: int | None = None, ranks: int = 0, sasa: bool = False):
+                 worker_groups: int | None = None, ranks: int = 0, sasa: bool = False,
+                 fused: bool = True, overlap: bool = True):
         self.heads, self.grid, self.d, self.block = heads, tuple(grid), d, block
         T, Y, X = self.grid
         self.n = T * Y * X
@@ -61,8 +65,8 @@ class FVAttnPath:
         self.v_tiles = can_tile if v_tiles is None else (v_tiles and can_tile)
         self.qh = torch.empty((H, n, d), dtype=dtype, device=dev)
         self.kh = torch.empty_like(self.qh)
-        self.vh = (torch.empty((H, nb, d, block), dtype=dtype, device=dev) if self.v_tiles
-                   else torch.empty_like(self.qh))
+        self._vh = (torch.empty((H, nb, d, block), dtype=dtype, device=dev) if self.v_tiles
+                    else torch.empty_like(self.qh))
         self.oh = torch.empty_like(self.qh)
         # tiles of two q-blocks share each K/V block load (tiled V only)
         self.group = (2 if self.v_tiles else 1) if group is None else group
@@ -77,6 +81,15 @@ class FVAttnPath:
         self.head_density = torch.empty(H, dtype=torch.float32, device=dev)
         self.route_ws = torch.empty(_lib.route_workspace_size(H, n, d, block),
                                     dtype=torch.uint8, device=dev)
+        # pooled block means, written by the Q/K gather when fused
+        self.fused = fused
+        if fused:
+            self.qbar = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
+            self.kbar = torch.empty_like(self.qbar)
+        # V layout on a side stream (default priority), joined before attention
+        self.overlap = overlap
+        self.side = torch.cuda.Stream(device=dev) if overlap else None
+        self._v_pending = False
         W = self.n_workers
         if worker_groups is None:
             # at least two heads per group, or the head-level LPT cannot balance
@@ -113,14 +126,48 @@ class FVAttnPath:
         self.ordered = True
 
     def to_hilbert(self, q, k, v):
-        _lib.permute_rows(q, self.qh, self.perm)
-        _lib.permute_rows(k, self.kh, self.perm)
-        if self.v_tiles:
-            _lib.pack_v(v, self.vh, self.perm, self.block)
+        if self.fused:
+            _lib.permute_pool(q, self.qh, self.perm, self.block, self.qbar)
+            _lib.permute_pool(k, self.kh, self.perm, self.block, self.kbar)
         else:
-            _lib.permute_rows(v, self.vh, self.perm)
+            _lib.permute_rows(q, self.qh, self.perm)
+            _lib.permute_rows(k, self.kh, self.perm)
+        if not self.overlap:
+            self._layout_v(v)
+            return
+        # the side stream first waits for all work queued so far on the main
+        # one: v is ready and the previous attention has finished reading vh
+        main = torch.cuda.current_stream(self.device)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            self._layout_v(v)
+        v.record_stream(self.side)
+        self._v_pending = True
+
+    def _layout_v(self, v):
+        if self.v_tiles:
+            _lib.pack_v(v, self._vh, self.perm, self.block)
+        else:
+            _lib.permute_rows(v, self._vh, self.perm)
+
+    @property
+    def vh(self):
+        """V in Hilbert order; reading it first joins the side stream."""
+        self.join()
+        return self._vh
+
+    def join(self):
+        """Make the main stream wait for the V layout (no-op without overlap)."""
+        if self._v_pending:
+            torch.cuda.current_stream(self.device).wait_stream(self.side)
+            self._v_pending = False
 
     def route(self, p: float, k_floor: int):
+        if self.fused:
+            _lib.route_pooled(self.qbar, self.kbar, self.n, self.block, p, k_floor, self.mask,
+                              self.kv_count, self.kv_index, self.head_load,
+                              self.head_density, self.route_ws)
+            return
         _lib.route(self.qh, self.kh, self.block, p, k_floor, self.mask, self.kv_count,
                    self.kv_index, self.head_load, self.head_density, self.route_ws)
 
@@ -154,6 +201,7 @@ class FVAttnPath:
         out: write O straight into `out` in token order (the kernels scatter
         rows through the Hilbert order); None: O stays in Hilbert order in
         self.oh."""
+        self.join()
         o = self.oh if out is None else out
         rows = None if out is None else self.perm
         if balanced:

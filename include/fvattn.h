@@ -153,6 +153,40 @@ int fvattn_route(const void* q, const void* k, int dtype, int heads, int n,
                  hipStream_t stream);
 
 /*
+ * Gather into Hilbert order fused with the routing's mean pooling: one read
+ * of the tensor gives both the reordered rows and the pooled block means
+ * (PaperDaily FVAttn article, method section: blocks formed along the Hilbert
+ * curve, importance from pooled Q/K; the overlap and fusion that keeps such
+ * bookkeeping off the critical path is in its section on the implementation
+ * and in the "Key findings" of the cere-bro FVAttn post).
+ *
+ * Computed, for src [heads][n][d] (bf16 or f32, device), index int32[n]:
+ *   dst[h][r][:] = src[h][index[r]][:]            (as fvattn_permute_rows)
+ *   pooled[h][j][c] = mean over the rows r of block j (r < n) of dst[h][r][c]
+ * pooled is fp32 [heads][nB][d], nB = ceil(n / block), caller-owned device
+ * memory; its values equal, bit for bit, the pooled means fvattn_route
+ * computes from dst (the same fp32 summation order).
+ * src and dst: 16-byte aligned, distinct (else FVATTN_EINVAL); limits as for
+ * fvattn_route: d <= 256, d % 8 == 0 (bf16) or d % 4 == 0 (f32), else
+ * FVATTN_EUNSUPPORTED.  Asynchronous on `stream`.
+ */
+int fvattn_permute_pool(const void* src, void* dst, const int32_t* index, int heads, int n,
+                        int d, int block, int dtype, float* pooled, hipStream_t stream);
+
+/*
+ * fvattn_route from given pooled means: qbar, kbar fp32 [heads][nB][d]
+ * (device; what fvattn_permute_pool writes for Q and K).  Everything after
+ * the pooling is the same computation, with the same outputs, limits
+ * (d % 4 == 0 here) and errors as fvattn_route.  workspace: at least
+ * fvattn_route_workspace_size(heads, n, d, block) bytes; the scores land in
+ * it where fvattn_route puts them, so fvattn_sasa_augment can read them.
+ */
+int fvattn_route_pooled(const float* qbar, const float* kbar, int heads, int n, int d,
+                        int block, float p, int k_floor, uint8_t* mask, int32_t* kv_count,
+                        int32_t* kv_index, int64_t* head_load, float* head_density,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * LPT work list over tiles for n_workers persistent workgroups.  A tile is
  * `group` consecutive q-blocks of one head (group 1 or 2): tile
  * t = h * ceil(n_qblocks / group) + m covers q-blocks [m*group,

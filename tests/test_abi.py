@@ -24,7 +24,7 @@ def test_library_is_built_in_tree():
 def test_exports_every_declared_symbol():
     lib = _lib.load_library()
     declared = _lib.declared_symbols()
-    assert len(declared) == 15, declared
+    assert len(declared) == 17, declared
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
@@ -67,6 +67,7 @@ def _validation_main():
     """Runs in a child process with no visible GPU."""
     lib = _lib.load_library()
     P = ctypes.c_void_p(4096)      # placeholder, never dereferenced
+    Q = ctypes.c_void_p(8192)      # a second one, where two must differ
     N = None
     EINVAL, EUNS, EWS = _lib.EINVAL, _lib.EUNSUPPORTED, _lib.EWORKSPACE
     checks = [
@@ -89,6 +90,26 @@ def _validation_main():
         (lib.fvattn_route(P, P, 1, 1, 4097 * 16, 64, 16, 0.9, 2, P, P, P, P, P, P, 1 << 30, N), EUNS),
         (lib.fvattn_route(P, P, 1, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, N, 1 << 30, N), EWS),
         (lib.fvattn_route(P, P, 1, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, P, 16, N), EWS),
+        # permute + pool
+        (lib.fvattn_permute_pool(P, P, P, 1, 128, 64, 16, 1, P, N), EINVAL),    # src == dst
+        (lib.fvattn_permute_pool(P, Q, P, 1, 128, 64, 16, 1, N, N), EINVAL),    # no pooled
+        (lib.fvattn_permute_pool(P, Q, N, 1, 128, 64, 16, 1, P, N), EINVAL),
+        (lib.fvattn_permute_pool(P, Q, P, 1, 128, 64, 16, 7, P, N), EINVAL),    # dtype
+        (lib.fvattn_permute_pool(P, Q, P, 1, 128, 64, 0, 1, P, N), EINVAL),
+        (lib.fvattn_permute_pool(ctypes.c_void_p(4104), Q, P, 1, 128, 64, 16, 1, P, N),
+         EINVAL),                                                               # unaligned
+        (lib.fvattn_permute_pool(P, Q, P, 1, 128, 264, 16, 1, P, N), EUNS),     # d > 256
+        (lib.fvattn_permute_pool(P, Q, P, 1, 128, 60, 16, 1, P, N), EUNS),      # bf16 d % 8
+        (lib.fvattn_permute_pool(P, Q, P, 1, 128, 62, 16, 0, P, N), EUNS),      # f32 d % 4
+        # route from pooled means
+        (lib.fvattn_route_pooled(P, P, 1, 128, 64, 16, 0.0, 2, P, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_route_pooled(P, P, 1, 128, 64, 16, 0.9, -1, P, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_route_pooled(N, P, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_route_pooled(P, P, 0, 128, 64, 16, 0.9, 2, P, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_route_pooled(P, P, 1, 128, 62, 16, 0.9, 2, P, P, P, P, P, P, 1 << 30, N), EUNS),
+        (lib.fvattn_route_pooled(P, P, 1, 4097 * 16, 64, 16, 0.9, 2, P, P, P, P, P, P, 1 << 30, N), EUNS),
+        (lib.fvattn_route_pooled(P, P, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, N, 1 << 30, N), EWS),
+        (lib.fvattn_route_pooled(P, P, 1, 128, 64, 16, 0.9, 2, P, P, P, P, P, P, 16, N), EWS),
         # schedule
         (lib.fvattn_schedule(P, 40, 591, 1, 2049, 0, P, P, P, P, P, 1 << 30, N), EUNS),
         (lib.fvattn_schedule(P, 40, 591, 1, 256, 2, P, P, P, P, P, 1 << 30, N), EINVAL),

@@ -1,0 +1,147 @@
+"""GPU parity of the fused Hilbert gather + pooling (fvattn_permute_pool), of
+routing from pooled means (fvattn_route_pooled), and of the two-stream path
+(V laid out on a second stream while routing and scheduling run) against
+the one-stream path, through the C ABI.
+
+The gather is checked bit for bit against the oracle's row permutation; the
+pooled means against the oracle's float64 means within the fp32 summation
+bound; the means, masks and kept lists bit for bit against the unfused GPU
+path (the same fp32 order by construction); the two-stream output bit for
+bit against the one-stream output over back-to-back steps with no
+synchronisation between them.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_11_amd import _lib, synth
+from block_sparse_attention_11_amd.pipeline import FVAttnPath
+from oracle import hilbert as ohb
+from oracle import route as ort
+from tests.test_gpu_parity import to_np, workload
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+U32 = 2.0 ** -24        # fp32 unit roundoff
+
+CASES = ["tiny", "small", "ragged_f32", "ragged_bf16", "mid_bf16", "mid_bf16_64"]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def hilbert_index(grid):
+    perm, _ = ohb.hilbert_order(*grid)
+    return perm, torch.from_numpy(perm.astype(np.int32)).to(DEV)
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_permute_pool_parity(name):
+    w = workload(name)
+    say(f"permute_pool {name}")
+    q, _, _, _ = synth.make_inputs(w, "cpu")
+    H, n, d = q.shape
+    nb = (n + w.block - 1) // w.block
+    perm_np, perm = hilbert_index(w.grid)
+    src = q.to(DEV)
+    dst = torch.zeros_like(src)
+    pooled = torch.full((H, nb, d), float("nan"), dtype=torch.float32, device=DEV)
+    _lib.permute_pool(src, dst, perm, w.block, pooled)
+    torch.cuda.synchronize()
+    want = ort.permute_rows(to_np(q).astype(np.float64), perm_np)
+    assert np.array_equal(to_np(dst), want.astype(to_np(dst).dtype))
+    ref = ort.pool_blocks(want, w.block)
+    # fp32 sum of m rows then one multiply: |err| <= (m + 1) u * mean |x|
+    absmean = ort.pool_blocks(np.abs(want), w.block)
+    got = pooled.cpu().numpy()
+    assert np.all(np.abs(got - ref) <= (w.block + 1) * U32 * absmean + 1e-30)
+    # bit for bit the means the unfused routing takes from the gathered rows
+    ws = torch.empty(_lib.route_workspace_size(H, n, d, w.block), dtype=torch.uint8,
+                     device=DEV)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    _lib.route(dst, dst, w.block, w.p, w.k, torch.empty((H, nb, nb), dtype=torch.uint8,
+               device=DEV), torch.empty((H, nb), **i32), torch.empty((H, nb, nb), **i32),
+               torch.empty(H, dtype=torch.int64, device=DEV),
+               torch.empty(H, dtype=torch.float32, device=DEV), ws)
+    torch.cuda.synchronize()
+    qbar = ws[:H * nb * d * 4].view(torch.float32).reshape(H, nb, d)
+    assert torch.equal(qbar, pooled)
+
+
+def test_permute_pool_single_row_blocks():
+    # block 1: every mean is the row itself, exactly
+    w = synth.Workload("b1", 2, 16, (2, 3, 5), 1, 0.9, 1, "f32")
+    q, _, _, _ = synth.make_inputs(w, "cpu")
+    perm_np, perm = hilbert_index(w.grid)
+    src = q.to(DEV)
+    dst = torch.empty_like(src)
+    pooled = torch.empty((2, 30, 16), dtype=torch.float32, device=DEV)
+    _lib.permute_pool(src, dst, perm, 1, pooled)
+    torch.cuda.synchronize()
+    assert torch.equal(pooled, dst)
+    assert np.array_equal(dst.cpu().numpy(), to_np(q)[:, perm_np, :])
+
+
+@pytest.mark.parametrize("name", ["small", "ragged_f32", "ragged_bf16", "mid_bf16"])
+def test_route_pooled_equals_route(name):
+    w = workload(name)
+    say(f"route_pooled vs route {name}")
+    q, k, v, _ = synth.make_inputs(w, "cpu")
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    outs = []
+    for fused in (True, False):
+        path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, n_workers=8,
+                          device=DEV, fused=fused, overlap=False)
+        path.order()
+        path.to_hilbert(q, k, v)
+        path.route(w.p, w.k)
+        torch.cuda.synchronize()
+        outs.append(path)
+    a, b = outs
+    assert torch.equal(a.qh, b.qh) and torch.equal(a.kh, b.kh)
+    assert torch.equal(a.mask, b.mask)
+    assert torch.equal(a.kv_count, b.kv_count)
+    assert torch.equal(a.head_load, b.head_load)
+    assert torch.equal(a.head_density, b.head_density)
+    cnt = a.kv_count.cpu().numpy()
+    ia, ib = a.kv_index.cpu().numpy(), b.kv_index.cpu().numpy()
+    for h in range(w.heads):
+        for i in range(a.nb):
+            assert ia[h, i, :cnt[h, i]].tolist() == ib[h, i, :cnt[h, i]].tolist()
+    # the scores land where the unfused routing puts them (SASA reads them)
+    nb, H = a.nb, w.heads
+    zs = 2 * ((4 * H * nb * w.d + 255) // 256 * 256)     # after the two pooled regions
+    za = a.route_ws[zs:zs + 4 * H * nb * nb]
+    zb = b.route_ws[zs:zs + 4 * H * nb * nb]
+    assert torch.equal(za, zb)
+
+
+@pytest.mark.parametrize("name,ranks,sasa", [("mid_bf16", 0, False), ("small", 0, False),
+                                             ("ragged_bf16", 0, False),
+                                             ("mid_bf16", 2, True)])
+def test_two_streams_match_one_stream(name, ranks, sasa):
+    """Back-to-back steps on different inputs with no synchronisation: the
+    V layout of step t+1 runs on the side stream and must wait for step t's
+    attention, and step t's attention for its own V layout."""
+    w = workload(name)
+    say(f"two streams {name} ranks={ranks} sasa={sasa}")
+    inputs = []
+    for seed in (1, 2, 3):
+        q, k, v, _ = synth.make_inputs(w, "cpu", seed=seed)
+        inputs.append((q.to(DEV), k.to(DEV), v.to(DEV)))
+    inputs.append(inputs[0])
+    kw = dict(dtype=inputs[0][0].dtype, device=DEV, ranks=ranks, sasa=sasa)
+    if ranks:
+        kw["n_workers"] = 8
+    one = FVAttnPath(w.heads, w.grid, w.d, w.block, overlap=False, **kw)
+    want = []
+    for q, k, v in inputs:
+        want.append(one.run(q, k, v, w.p, w.k))
+        torch.cuda.synchronize()
+    two = FVAttnPath(w.heads, w.grid, w.d, w.block, overlap=True, **kw)
+    got = [two.run(q, k, v, w.p, w.k) for q, k, v in inputs]
+    torch.cuda.synchronize()
+    for i, (g, r) in enumerate(zip(got, want)):
+        assert torch.equal(g, r), f"step {i}"

@@ -101,10 +101,11 @@ def test_pack_v_bit_exact(d, block, n):
 # ---------------------------------------------------------------------------
 # Routing
 # ---------------------------------------------------------------------------
-def run_route(w, q, k, p, kf):
-    """GPU route on Hilbert-ordered inputs; returns numpy outputs + the
-    Hilbert-ordered float64 inputs for the oracle."""
-    path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, n_workers=8, device=DEV)
+def run_route(w, q, k, p, kf, fused=True):
+    """GPU gather + route; fused: pooling in the gather (permute_pool +
+    route_pooled), else permute_rows + route."""
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, n_workers=8, device=DEV,
+                      fused=fused)
     path.order()
     path.to_hilbert(q, k, k)
     path.route(p, kf)
@@ -143,14 +144,15 @@ def workload(name):
     raise KeyError(name)
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
 @pytest.mark.parametrize("name,p,kf", ROUTE_CASES)
-def test_route_parity(name, p, kf):
+def test_route_parity(name, p, kf, fused):
     w = workload(name)
     p = w.p if p is None else p
     kf = w.k if kf is None else kf
-    say(f"route {name} p={p} k={kf}")
+    say(f"route {name} p={p} k={kf} fused={fused}")
     q, k, v, _ = synth.make_inputs(w, "cpu")
-    path = run_route(w, q.to(DEV), k.to(DEV), p, kf)
+    path = run_route(w, q.to(DEV), k.to(DEV), p, kf, fused)
     perm, _ = ohb.hilbert_order(*w.grid)
     assert np.array_equal(path.perm.cpu().numpy(), perm)
     qh = ort.permute_rows(to_np(q).astype(np.float64), perm)
@@ -158,10 +160,17 @@ def test_route_parity(name, p, kf):
     # the GPU's Hilbert-ordered copies are the same bytes
     assert np.array_equal(to_np(path.qh), qh.astype(to_np(path.qh).dtype))
     ora = ort.route(qh, kh, w.block, p, kf)
+    assert np.array_equal(to_np(path.kh), kh.astype(to_np(path.kh).dtype))
     ws = path.route_ws
     nb, H, d = path.nb, w.heads, w.d
-    qbar = ws[:H * nb * d * 4].view(torch.float32).reshape(H, nb, d).cpu().numpy()
+    if fused:
+        qbar, kbar = path.qbar.cpu().numpy(), path.kbar.cpu().numpy()
+    else:
+        qbar = ws[:H * nb * d * 4].view(torch.float32).reshape(H, nb, d).cpu().numpy()
+        kbar = None
     assert np.allclose(qbar, ora["qbar"], rtol=1e-5, atol=1e-6)
+    if kbar is not None:
+        assert np.allclose(kbar, ora["kbar"], rtol=1e-5, atol=1e-6)
     gc = path.kv_count.cpu().numpy()
     gi = path.kv_index.cpu().numpy()
     stats, bad = classify_rows(ora["P"], p, kf, gc, gi, ora["kv_count"], ora["kv_index"])
