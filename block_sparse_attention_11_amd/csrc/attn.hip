@@ -1100,12 +1100,16 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
         }
         if (r0 + half * HK + HK > n) {
           keep_branch();
+          // keys at or past n get -inf; the sign of key - n selects, so the
+          // mask needs no per-element condition registers
+          const int base = r0 + half * HK + 4 * g - n;
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-              const int key = r0 + half * HK + 32 * kt + 8 * (e >> 2) + 4 * g + (e & 3);
-              if (key >= n) s[kt][e] = -INFINITY;
+              const int keep = (base + 32 * kt + 8 * (e >> 2) + (e & 3)) >> 31;  // -1: key < n
+              s[kt][e] = __uint_as_float((__float_as_uint(s[kt][e]) & (uint32_t)keep) |
+                                         (0xff800000u & ~(uint32_t)keep));
             }
         }
         float mx = -INFINITY;
