@@ -141,7 +141,10 @@ class FVAttnPath:
         self.side.wait_stream(main)
         with torch.cuda.stream(self.side):
             self._layout_v(v)
-        v.record_stream(self.side)
+        if not torch.cuda.is_current_stream_capturing():
+            # keep v's memory for the side stream's read (a captured graph
+            # holds its inputs itself)
+            v.record_stream(self.side)
         self._v_pending = True
 
     def _layout_v(self, v):
