@@ -379,6 +379,34 @@ def main():
         _, _, st_static = run_steps(path, q, k, v, o2, w.p, w.k, max(2, args.dense_steps), 1,
                                     runtime=False)
         imb_static = cu_imbalance(path.timing.cpu().numpy())
+        log("graph replay control")
+        # the same step captured once in a HIP graph and replayed: no host
+        # launch work per step (the library allocates and synchronises nothing)
+        og = torch.empty_like(q)
+        sw = torch.cuda.Stream()
+        sw.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(sw):
+            path.order()
+            path.run(q, k, v, w.p, w.k, out=og)
+        torch.cuda.current_stream().wait_stream(sw)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            path.order()                  # the timed step's work, Hilbert order included
+            path.run(q, k, v, w.p, w.k, out=og)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = max(2, args.dense_steps)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / reps
+        graph_equal = bool(torch.equal(og, out))
+        del graph, og
         log("one-stream unfused control")
         p1 = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=dt, n_workers=path.n_workers,
                         device="cuda", group=args.group or None, fused=False, overlap=False)
@@ -396,6 +424,8 @@ def main():
             "dense_attention_ms": round(st_dense["attention"], 4),
             "dense_tflops": round(dense_flops / (st_dense["attention"] * 1e-3) / 1e12, 2),
             "speedup_vs_dense_attention": round(st_dense["attention"] / attn_ms, 4),
+            "graph_replay_step_ms": round(graph_ms, 4),
+            "graph_replay_equals_eager": graph_equal,
             "one_stream_unfused_step_ms": round(step1_ms, 4),
             "one_stream_unfused_stages_ms": {k2: round(v2, 4) for k2, v2 in st1.items()},
             "step_ms": round(step_ms, 4),
