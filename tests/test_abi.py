@@ -205,3 +205,13 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(ValueError):
         _lib.hilbert_permute(1, 2, 2, x, x)
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/fvattn.h compiles as C99 (a C caller needs no C++)."""
+    src = tmp_path / "use.c"
+    src.write_text('#include "fvattn.h"\nint main(void) { return fvattn_version() < 0; }\n')
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                          "-D__HIP_PLATFORM_AMD__", f"-I{os.path.join(ROOT, 'include')}",
+                          "-I/opt/rocm/include", str(src)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
