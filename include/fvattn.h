@@ -158,7 +158,8 @@ int fvattn_route(const void* q, const void* k, int dtype, int heads, int n,
  * (PaperDaily FVAttn article, method section: blocks formed along the Hilbert
  * curve, importance from pooled Q/K; the overlap and fusion that keeps such
  * bookkeeping off the critical path is in its section on the implementation
- * and in the "Key findings" of the cere-bro FVAttn post).
+ * and in the "Key findings" of the wiki post "FVAttn: Adaptive Sparse Attention
+ * with Runtime Load Balancing").
  *
  * Computed, for src [heads][n][d] (bf16 or f32, device), index int32[n]:
  *   dst[h][r][:] = src[h][index[r]][:]            (as fvattn_permute_rows)
