@@ -1052,13 +1052,17 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
     const Walk nxt = advance(cur);
     wait_vmcnt<0>();
     lds_barrier();
-    if (nxt.it < end) dma(kn, vn, nxt.h, nxt.u);
+    // the next block's copies: wavefronts with nothing to compute this step
+    // issue their share now, the others after their first S product, so the
+    // copies do not compete with the step's first LDS reads (the buffers
+    // they fill were released by the barrier above)
+    const bool mine = grp == 0 ? cur.ina : cur.inb;
+    if (!mine && nxt.it < end) dma(kn, vn, nxt.h, nxt.u);
     if (dyn && cur.first && wave == 0) {
       // the tile two ahead of this one; its slot was last read two tiles ago
       const int c = claim();
       if (lane == 0) mbox[(cur.ord + 2) & 3] = c;
     }
-    const bool mine = grp == 0 ? cur.ina : cur.inb;
     if (mine) {
       // the block in halves of HK keys: an online-softmax step per half keeps
       // the live score / probability registers small
@@ -1098,6 +1102,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
           }
           __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
         }
+        if (half == 0 && nxt.it < end) dma(kn, vn, nxt.h, nxt.u);
         if (r0 + half * HK + HK > n) {
           keep_branch();
           // keys at or past n get -inf; the sign of key - n selects, so the
