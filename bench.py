@@ -1,17 +1,21 @@
 """Benchmark of the FVAttn hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input that
-is already resident in HBM: Hilbert order, Q/K/V permute, routing (pooled
-Q/K, Top-p + Top-k), LPT schedule, persistent block-sparse attention, O
-permute back.
+is already resident in HBM: Hilbert order, Q/K gather into that order with
+the block pooling in the same pass, V packed into key-block tiles on a
+second stream, routing (pooled Q/K, Top-p + Top-k), LPT schedule, and the
+persistent block-sparse attention, which stores O back in token order.
 
 Prints ONE JSON line.  `value` = kept-block FLOPs (sum over kept (h, i, j) of
 4 * n_i * n_j * d, true block sizes) per second of the whole step, in
-TFLOP/s.  The attention-only rate, the dense (p = 1) control and its
-speedup, the head-major (unbalanced) control, per-CU busy-time imbalance,
-the attention kernel's roofline and the CPU oracle baseline ride along.
+TFLOP/s.  The attention-only rate, the attention kernel's roofline, per-CU
+busy-time imbalance, the controls (head-major grid launch, static LPT
+without claims, the step as one replayed HIP graph, the one-stream unfused
+path, dense p = 1) and the CPU oracle baseline ride along; --sasa adds the
+per-rank SASA report.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p]
+                       [--sasa] [--no-controls] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
