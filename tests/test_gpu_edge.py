@@ -62,3 +62,30 @@ def test_degenerate_path(name):
     out2 = path.run(q, k, v, w.p, w.k)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
+
+
+# every MFMA instance of the pair kernel (d, block) through the whole path,
+# with a ragged tail and an odd number of q-blocks
+SHAPES = [
+    ("d64_b128", W("d64_b128", 3, 64, (3, 9, 13), 128, 0.9, 2, "bf16", s_range=(2.0, 64.0))),
+    ("d128_b64", W("d128_b64", 3, 128, (3, 9, 13), 64, 0.9, 2, "bf16", s_range=(2.0, 64.0))),
+    ("d64_b64", W("d64_b64", 2, 64, (2, 7, 19), 64, 0.85, 3, "bf16", s_range=(2.0, 64.0))),
+    ("d128_b128", W("d128_b128", 2, 128, (2, 11, 17), 128, 0.85, 3, "bf16",
+                    s_range=(2.0, 64.0))),
+]
+
+
+@pytest.mark.parametrize("name,w", SHAPES, ids=[s[0] for s in SHAPES])
+@pytest.mark.parametrize("ranks", [0, 2])
+def test_every_mfma_shape(name, w, ranks):
+    say(f"shape {name}: grid {w.grid}, d={w.d}, block={w.block}, ranks={ranks}")
+    q, k, v, _ = synth.make_inputs(w, DEV)
+    kw = dict(ranks=ranks, n_workers=8) if ranks else {}
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, device=DEV, **kw)
+    out = path.run(q, k, v, w.p, w.k)
+    torch.cuda.synchronize()
+    check_route(path, w, w.p, range(w.heads))
+    if not ranks:
+        check_schedule(path)
+    tiles = [(h, i) for h in range(w.heads) for i in range(path.nb)]
+    check_attention(path, w, v, out, tiles)
