@@ -239,6 +239,42 @@ def sasa_report(w, q, k, v, steps: int, warmup: int, dense_out=None, default_out
     return rep
 
 
+def load_shift_report(w, steps: int = 4, ranks: int = XCDS):
+    """Per-head and per-rank kept-block loads over `steps` denoising steps
+    (s_h, K, E, V redrawn per step, radii fixed), routed by the library; the
+    largest relative change of a head's and of a rank's load between adjacent
+    steps, and each step's rank imbalance (max/mean).  Ranks hold contiguous
+    head shards (head h on rank h*R/H), as sequence parallelism places them."""
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, device="cuda")
+    loads, dens = [], []
+    for step, r0 in synth.long_steps(w, steps):
+        q, k, v, _ = synth.make_inputs(w.with_(seed=step), "cuda", r_override=r0)
+        path.order()
+        path.to_hilbert(q, k, v)
+        path.route(w.p, w.k)
+        torch.cuda.synchronize()
+        loads.append(path.head_load.cpu().numpy().astype(np.float64))
+        dens.append(path.head_density.cpu().numpy())
+        del q, k, v
+    group = np.array([h * ranks // w.heads for h in range(w.heads)])
+    rank_loads = [np.bincount(group, weights=l, minlength=ranks) for l in loads]
+    def change(series, ref):
+        # largest |b - a| / ref(a, b) over the heads (or ranks), per step pair
+        return [round(float(np.max(np.abs(b - a) / np.maximum(ref(a, b), 1.0))), 4)
+                for a, b in zip(series, series[1:])]
+    prev = lambda a, b: a                       # noqa: E731
+    larger = lambda a, b: np.maximum(a, b)      # noqa: E731
+    return {"workload": w.name, "steps": steps, "ranks": ranks,
+            "density_mean_min_max": [[round(float(d.mean()), 4), round(float(d.min()), 4),
+                                      round(float(d.max()), 4)] for d in dens],
+            "max_head_load_change_of_larger": change(loads, larger),
+            "max_rank_load_change_of_larger": change(rank_loads, larger),
+            "max_head_load_change_of_previous": change(loads, prev),
+            "max_rank_load_change_of_previous": change(rank_loads, prev),
+            "rank_imbalance_max_over_mean": [round(float(r.max() / r.mean()), 4)
+                                             for r in rank_loads]}
+
+
 def cpu_baseline(q, k, v, w, budget_s=15.0, max_tiles=400):
     """The float64 oracle, untuned, on one head of the same workload: Hilbert
     order, permute, routing for that head, then block-sparse attention on as
@@ -298,6 +334,8 @@ def main():
     ap.add_argument("--no-controls", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--load-shift", action="store_true",
+                    help="add the step-to-step head / rank load change over 4 steps")
     ap.add_argument("--sasa", action="store_true",
                     help="also report the per-rank image on the 8 XCD groups with and "
                          "without slack-aware sparse augmentation")
@@ -441,6 +479,9 @@ def main():
                       "pages_dit_speedup_8xH20": "2.02-2.11",
                       "pages_imbalance_before_after_rlb_8xH20": "1.34 -> 1.08",
                       "pages_attention_share_of_generation_1xH20": 0.741}
+    if args.load_shift:
+        log("load shift over steps")
+        res["load_shift"] = load_shift_report(w)
     if args.sasa:
         res["sasa"] = sasa_report(w, q, k, v, max(2, args.dense_steps), 1,
                                   dense_out=None if args.no_controls else o2,

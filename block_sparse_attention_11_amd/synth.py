@@ -83,6 +83,13 @@ WORKLOADS = {
                             flat_heads=tuple(range(32, 40)), flat_s=64.0,
                             note="supplementary: 720p shape with s_h log-uniform"
                                  " in [64, 1024], heads 32-39 at s=64 (dense, heavy)"),
+    # Supplementary, labelled: the long shape with the same strong coupling,
+    # s_h (and K, E, V) redrawn every step, so per-head loads move between steps.
+    "long720p_sparse": Workload("long720p_sparse", 40, 128, (41, 45, 80), 128, 0.95, 8,
+                                "bf16", s_range=(64.0, 1024.0),
+                                flat_heads=tuple(range(32, 40)), flat_s=64.0,
+                                note="supplementary: long720p shape with s_h log-uniform"
+                                     " in [64, 1024] redrawn per step, heads 32-39 at s=64"),
     # One rank's share of the 720p workload under 8-way head sharding.
     "720p_rank": Workload("720p_rank", 5, 128, (21, 45, 80), 128, 0.95, 8, "bf16",
                           note="720p, 5 of 40 heads (one of 8 ranks)"),

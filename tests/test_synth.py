@@ -29,6 +29,8 @@ def test_workload_sizes():
     assert (W["720p"].n, W["720p"].n_blocks) == (75600, 591)
     assert (W["480p"].n, W["480p"].n_blocks) == (32760, 256)
     assert (W["long720p"].n, W["long720p"].n_blocks) == (147600, 1154)
+    assert (W["long720p_sparse"].n, W["long720p_sparse"].n_blocks) == (147600, 1154)
+    assert W["long720p_sparse"].flat_heads == tuple(range(32, 40))
     assert W["tiny"].n_blocks == 8 and W["small"].n_blocks == 16
 
 
