@@ -204,10 +204,12 @@ def sasa_report(w, q, k, v, steps: int, warmup: int, dense_out=None, default_out
     rep = {"groups": G, "workload": w.name}
     if default_out is not None:
         rep["default_path_rel_l2_vs_dense"] = rel_l2(default_out, dense_out)
-    for name, aug in (("no_sasa", False), ("sasa", True)):
+    # the pages' n1 = 0.8, and a derated n1 for groups that share one card
+    for name, aug, n1 in (("no_sasa", False, 0.8), ("sasa", True, 0.8),
+                          ("sasa_n1_0.4", True, 0.4)):
         log(f"per-rank image, {name}")
         path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, device="cuda",
-                          ranks=G, sasa=aug)
+                          ranks=G, sasa=aug, sasa_n1=n1)
         o = torch.empty_like(q)
         _, step_ms, stages = run_steps(path, q, k, v, o, w.p, w.k, steps, warmup)
         info = path.sasa_info.cpu().numpy()
@@ -236,6 +238,10 @@ def sasa_report(w, q, k, v, steps: int, warmup: int, dense_out=None, default_out
                                        rep["no_sasa"]["attention_ms"], 4)
     rep["sasa_rel_l2_ratio"] = round(rep["sasa"]["rel_l2_vs_dense"] /
                                      max(rep["no_sasa"]["rel_l2_vs_dense"], 1e-300), 4)
+    rep["sasa_n1_0.4_makespan_ratio"] = round(rep["sasa_n1_0.4"]["attention_ms"] /
+                                              rep["no_sasa"]["attention_ms"], 4)
+    rep["sasa_n1_0.4_rel_l2_ratio"] = round(rep["sasa_n1_0.4"]["rel_l2_vs_dense"] /
+                                            max(rep["no_sasa"]["rel_l2_vs_dense"], 1e-300), 4)
     return rep
 
 

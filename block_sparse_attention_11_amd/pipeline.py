@@ -45,7 +45,8 @@ class FVAttnPath:
                  n_workers: int | None = None, device="cuda", tile_order: bool = False,
                  v_tiles: bool | None = None, group: int | None = None,
                  worker_groups: int | None = None, ranks: int = 0, sasa: bool = False,
-                 fused: bool = True, overlap: bool = True):
+                 fused: bool = True, overlap: bool = True,
+                 sasa_n1: float = _lib.SASA_N1):
         self.heads, self.grid, self.d, self.block = heads, tuple(grid), d, block
         T, Y, X = self.grid
         self.n = T * Y * X
@@ -110,6 +111,8 @@ class FVAttnPath:
         if ranks > 1 and (ranks > min(64, W) or W % ranks != 0):
             raise ValueError("ranks must divide the worker count and be <= 64")
         self.ranks, self.sasa = ranks, sasa
+        # SASA's augmentation coefficient (the pages' n1 = 0.8 by default)
+        self.sasa_n1 = sasa_n1
         if ranks > 1:
             i64 = dict(dtype=torch.int64, device=dev)
             self.head_group = torch.empty(H, **i32)
@@ -178,7 +181,7 @@ class FVAttnPath:
         """Per-rank image: mode, head moves and budgets; with sasa, the extra
         blocks (rewrites mask, kv lists, head load and density)."""
         _lib.sasa_plan(self.head_load, self.ranks, self.head_group, self.group_budget,
-                       self.sasa_info)
+                       self.sasa_info, n1=self.sasa_n1)
         if self.sasa:
             _lib.sasa_augment(self.route_ws, self.heads, self.n, self.d, self.block,
                               self.head_group, self.group_budget, self.mask, self.kv_count,
