@@ -17,8 +17,11 @@
 //                  reads Q and K exactly once.
 //   score_kernel   z = qbar kbar^T * scale per head, LDS-tiled 64x64 fp32.
 //   select_kernel  one workgroup per (query block, head): row softmax, bitonic
-//                  sort of (P, ~j) keys in LDS, workgroup prefix sum, cut,
-//                  mask row and ascending kept list via a flag scan.
+//                  sort of (P, ~j) keys held in registers (partners in the
+//                  same thread swap in place, partners in the wavefront come
+//                  by lane shuffle, only the widest stages go through LDS),
+//                  workgroup prefix sum, cut, mask row and ascending kept
+//                  list via a flag scan.
 //   load_kernel    per-head sum of kv_count (exact int64) and density.
 #include <math.h>
 
@@ -190,6 +193,8 @@ __global__ __launch_bounds__(256) void score_kernel(
 // One workgroup per row (i = blockIdx.x, h = blockIdx.y).  Dynamic LDS:
 // np uint64 sort keys + np floats (prefix sums) + np ints (flags/positions),
 // np = next power of two >= nb.
+// KP = np / kSelectThreads keys per thread (thread t holds ranks KP*t ..).
+template <int KP>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     const float* __restrict__ z, int nb, int np, float p, int k_floor,
     uint8_t* __restrict__ mask, int32_t* __restrict__ kv_count,
@@ -218,33 +223,76 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
   }
   // deterministic order: per-thread strided partials, then a fixed tree
   sum = block_reduce<kSelectThreads>(sum, s_redf, [](float a, float b) { return a + b; });
-  for (int j = tid; j < np; j += kSelectThreads) {
-    if (j < nb) {
-      const float pj = cum[j] / sum;
-      keys[j] = ((uint64_t)__float_as_uint(pj) << 32) | (uint64_t)(~(uint32_t)j);
-    } else {
-      keys[j] = 0;                   // sorts after every real key
-    }
+  __syncthreads();                   // cum[] is read across threads below
+  uint64_t kr[KP];
+#pragma unroll
+  for (int e = 0; e < KP; ++e) {
+    const int j = KP * tid + e;
+    // (P, ~j): P descending, then j ascending; padding (0) sorts last
+    kr[e] = j < nb ? ((uint64_t)__float_as_uint(cum[j] / sum) << 32) | (uint64_t)(~(uint32_t)j)
+                   : 0;
   }
-  __syncthreads();
 
-  // bitonic sort, descending
+  // bitonic sort, descending.  A stage pairs rank x with x ^ jj; the lower
+  // rank takes the larger key where (x & kk) == 0, the smaller elsewhere.
+  // Partners in this thread's registers swap in place, partners in this
+  // wavefront come by lane shuffle, others through LDS (one barrier each).
   for (int kk = 2; kk <= np; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int x = tid; x < np; x += kSelectThreads) {
-        const int y = x ^ jj;
-        if (y > x) {
-          const uint64_t a = keys[x], b = keys[y];
-          const bool desc = (x & kk) == 0;
-          if (desc ? (a < b) : (a > b)) {
-            keys[x] = b;
-            keys[y] = a;
+    int jj = kk >> 1;
+    if (jj >= 64 * KP) {
+#pragma unroll
+      for (int e = 0; e < KP; ++e) keys[KP * tid + e] = kr[e];
+      __syncthreads();
+      for (; jj >= 64 * KP; jj >>= 1) {
+        for (int x = tid; x < np; x += kSelectThreads) {
+          const int y = x ^ jj;
+          if (y > x) {
+            const uint64_t a = keys[x], b = keys[y];
+            const bool desc = (x & kk) == 0;
+            if (desc ? (a < b) : (a > b)) {
+              keys[x] = b;
+              keys[y] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int e = 0; e < KP; ++e) kr[e] = keys[KP * tid + e];
+    }
+    for (; jj >= KP; jj >>= 1) {
+      const int lanes = jj / KP;       // partner thread tid ^ lanes, same wavefront
+#pragma unroll
+      for (int e = 0; e < KP; ++e) {
+        const int x = KP * tid + e;
+        const uint64_t mine = kr[e];
+        const uint64_t other = (uint64_t)__shfl_xor((long long)mine, lanes, kWave);
+        const bool keep_max = ((x & jj) == 0) == ((x & kk) == 0);
+        kr[e] = keep_max ? (mine > other ? mine : other) : (mine < other ? mine : other);
+      }
+    }
+    // in-register stages jr = min(jj, KP/2) .. 1 (compile-time register indices)
+#pragma unroll
+    for (int jr = KP / 2; jr >= 1; jr >>= 1) {
+      if (jr <= jj) {
+#pragma unroll
+        for (int e = 0; e < KP; ++e) {
+          if ((e & jr) == 0) {
+            const int x = KP * tid + e;
+            const uint64_t a = kr[e], b = kr[e | jr];
+            const bool desc = (x & kk) == 0;
+            if (desc ? (a < b) : (a > b)) {
+              kr[e] = b;
+              kr[e | jr] = a;
+            }
           }
         }
       }
-      __syncthreads();
     }
   }
+#pragma unroll
+  for (int e = 0; e < KP; ++e) keys[KP * tid + e] = kr[e];
+  __syncthreads();
 
   // inclusive prefix sum of P in ranked order: contiguous per-thread chunks
   const int per = np / kSelectThreads > 0 ? np / kSelectThreads : 1;
@@ -263,8 +311,18 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     float* tot = reinterpret_cast<float*>(flag);   // reuse as scratch
     tot[tid] = run;
     __syncthreads();
-    float base = 0.f;
-    for (int t = 0; t < tid; ++t) base += tot[t];
+    if (tid == 0) {
+      // all prefixes left to right in one thread: base(t) = ((tot[0] + tot[1])
+      // + ...) + tot[t-1], the sum each thread would form for itself
+      float b = 0.f;
+      for (int t = 0; t < kSelectThreads; ++t) {
+        const float v = tot[t];
+        tot[t] = b;
+        b += v;
+      }
+    }
+    __syncthreads();
+    const float base = tot[tid];
     __syncthreads();
     for (int e = 0; e < per; ++e) {
       const int x = c0 + e;
@@ -402,8 +460,29 @@ hipError_t launch_route_pooled(const float* qbar, const float* kbar, int heads, 
   while (np < nb) np <<= 1;
   if (np < kSelectThreads) np = kSelectThreads;
   const size_t lds = (size_t)np * (sizeof(uint64_t) + sizeof(float) + sizeof(int32_t));
-  hipLaunchKernelGGL(select_kernel, dim3(nb, heads), dim3(kSelectThreads), lds, s,
-                     ws.z, nb, np, p, k_floor, mask, kv_count, kv_index);
+  const dim3 grid(nb, heads);
+  switch (np / kSelectThreads) {
+    case 1:
+      hipLaunchKernelGGL(select_kernel<1>, grid, dim3(kSelectThreads), lds, s, ws.z, nb, np, p,
+                         k_floor, mask, kv_count, kv_index);
+      break;
+    case 2:
+      hipLaunchKernelGGL(select_kernel<2>, grid, dim3(kSelectThreads), lds, s, ws.z, nb, np, p,
+                         k_floor, mask, kv_count, kv_index);
+      break;
+    case 4:
+      hipLaunchKernelGGL(select_kernel<4>, grid, dim3(kSelectThreads), lds, s, ws.z, nb, np, p,
+                         k_floor, mask, kv_count, kv_index);
+      break;
+    case 8:
+      hipLaunchKernelGGL(select_kernel<8>, grid, dim3(kSelectThreads), lds, s, ws.z, nb, np, p,
+                         k_floor, mask, kv_count, kv_index);
+      break;
+    default:                            // nB <= 4096: at most 16 keys per thread
+      hipLaunchKernelGGL(select_kernel<16>, grid, dim3(kSelectThreads), lds, s, ws.z, nb, np,
+                         p, k_floor, mask, kv_count, kv_index);
+      break;
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_head_load(kv_count, heads, nb, head_load, head_density, s);
