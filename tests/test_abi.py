@@ -125,6 +125,8 @@ def _validation_main():
         (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 256, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EUNS),
+        # tiled K/V one head past 2^31 bytes (17 heads x 4095 blocks of 128 x 128)
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 17, 4095 * 128, 128, 128, 1, 2, 0.0, P, P, N, N, 0, N, N, 0, N, N), EUNS),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, float("inf"), P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, N, 4, N, N, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, P, 0, N, N, 0, N, N), EINVAL),

@@ -216,6 +216,7 @@ SCHED_CASES = [
     ("max_workers", None, 2048),
     ("random_odd", None, 100),
     ("big_costs", None, 256),
+    ("max_heads", None, 256),        # the most heads the two-level schedule takes
 ]
 
 
@@ -237,6 +238,8 @@ def test_schedule_bit_exact(name, costs, W, tile_order, group, xg):
         costs = rng.integers(8, 1155, size=(40, 1154))
     elif name == "big_costs":
         costs = rng.integers(0, 16384, size=(5, 333))
+    elif name == "max_heads":
+        costs = rng.integers(0, 50, size=(4096, 3))
     got = gpu_schedule(costs, W, tile_order, group, X)
     gc = olpt.group_costs(costs, group)
     if X > 1:
