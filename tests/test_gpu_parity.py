@@ -39,7 +39,10 @@ def to_np(t):
 # ---------------------------------------------------------------------------
 GRIDS = [(1, 1, 1), (1, 1, 5), (2, 2, 2), (2, 8, 8), (3, 5, 7), (17, 1, 3),
          (4, 16, 16), (16, 16, 16), (21, 30, 52), (21, 45, 80), (41, 45, 80),
-         (1, 300, 2), (33, 17, 65)]
+         (1, 300, 2), (33, 17, 65),
+         # sides up to the largest the ABI takes (1024: 10 bits per axis)
+         (1024, 1, 1), (1, 1, 1024), (3, 1024, 7), (1, 1024, 1024), (1024, 1024, 1),
+         (513, 1000, 3)]
 
 
 @pytest.mark.parametrize("grid", GRIDS)
