@@ -145,3 +145,27 @@ def test_two_streams_match_one_stream(name, ranks, sasa):
     torch.cuda.synchronize()
     for i, (g, r) in enumerate(zip(got, want)):
         assert torch.equal(g, r), f"step {i}"
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 8), (torch.bfloat16, 256),
+                                     (torch.float32, 4), (torch.float32, 256)])
+def test_permute_pool_row_widths(dtype, d):
+    """The narrowest and widest rows fvattn_permute_pool takes (bf16: d % 8,
+    f32: d % 4, d <= 256), on a ragged Hilbert grid with several blocks."""
+    grid, block, H = (3, 7, 11), 64, 3
+    say(f"permute_pool widths {dtype} d={d}")
+    n = grid[0] * grid[1] * grid[2]
+    nb = (n + block - 1) // block
+    g = torch.Generator().manual_seed(d)
+    src_cpu = (torch.randn((H, n, d), generator=g) * 3).to(dtype)
+    perm_np, perm = hilbert_index(grid)
+    dst = torch.zeros((H, n, d), dtype=dtype, device=DEV)
+    pooled = torch.full((H, nb, d), float("nan"), dtype=torch.float32, device=DEV)
+    _lib.permute_pool(src_cpu.to(DEV), dst, perm, block, pooled)
+    torch.cuda.synchronize()
+    want = ort.permute_rows(to_np(src_cpu).astype(np.float64), perm_np)
+    assert np.array_equal(to_np(dst), want.astype(to_np(dst).dtype))
+    ref = ort.pool_blocks(want, block)
+    absmean = ort.pool_blocks(np.abs(want), block)
+    got = pooled.cpu().numpy()
+    assert np.all(np.abs(got - ref) <= (block + 1) * U32 * absmean + 1e-30)

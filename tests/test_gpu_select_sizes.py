@@ -34,24 +34,24 @@ def say(msg):
     print(msg, flush=True)
 
 
-def pooled_inputs(nb, heads, seed):
+def pooled_inputs(nb, heads, seed, d=D):
     g = np.random.default_rng(seed)
-    qbar = g.standard_normal((heads, nb, D)).astype(np.float32)
-    kbar = g.standard_normal((heads, nb, D)).astype(np.float32)
+    qbar = g.standard_normal((heads, nb, d)).astype(np.float32)
+    kbar = g.standard_normal((heads, nb, d)).astype(np.float32)
     # row scales 0.05 .. 8: from nearly uniform importances to a few dominant blocks
     scale = np.exp(g.uniform(math.log(0.05), math.log(8.0), (heads, nb, 1)))
     return (qbar * scale).astype(np.float32), kbar
 
 
 def run(qbar, kbar, n, p, k):
-    H, nb, _ = qbar.shape
+    H, nb, d = qbar.shape
     i32 = dict(dtype=torch.int32, device=DEV)
     out = dict(mask=torch.empty((H, nb, nb), dtype=torch.uint8, device=DEV),
                kv_count=torch.empty((H, nb), **i32),
                kv_index=torch.empty((H, nb, nb), **i32),
                head_load=torch.empty(H, dtype=torch.int64, device=DEV),
                head_density=torch.empty(H, dtype=torch.float32, device=DEV))
-    ws = torch.empty(_lib.route_workspace_size(H, n, D, BLOCK), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(_lib.route_workspace_size(H, n, d, BLOCK), dtype=torch.uint8, device=DEV)
     _lib.route_pooled(torch.from_numpy(qbar).to(DEV), torch.from_numpy(kbar).to(DEV), n,
                       BLOCK, p, k, out["mask"], out["kv_count"], out["kv_index"],
                       out["head_load"], out["head_density"], ws)
@@ -81,13 +81,17 @@ def check_consistent(r, nb, k):
     return H
 
 
-@pytest.mark.parametrize("nb", NBS)
-def test_select_size_classes(nb):
+CASES = [(nb, D) for nb in NBS] + [(3, 4), (591, 4), (3, 256), (591, 256), (2049, 256)]
+
+
+@pytest.mark.parametrize("nb,d", CASES)
+def test_select_size_classes(nb, d):
+    """d from the smallest (4) to the largest (256) pooled width the ABI takes."""
     heads = 2 if nb <= 1024 else 1
     n = nb * BLOCK - (5 if nb > 1 else 3)          # ragged last block
     p, k = 0.9, 4
-    say(f"select nB={nb} heads={heads} n={n} p={p} k={k}")
-    qbar, kbar = pooled_inputs(nb, heads, seed=nb)
+    say(f"select nB={nb} d={d} heads={heads} n={n} p={p} k={k}")
+    qbar, kbar = pooled_inputs(nb, heads, seed=nb + d, d=d)
     r = run(qbar, kbar, n, p, k)
     check_consistent(r, nb, k)
     g = np.random.default_rng(1000 + nb)
