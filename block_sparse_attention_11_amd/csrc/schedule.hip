@@ -42,7 +42,13 @@
 //   head_group_kernel      head loads, heads sorted by (load desc, id asc)
 //                          in LDS, greedy over the groups in one wavefront
 //   group_partition_kernel stable split of the LPT order by group
-//   lpt_assign_kernel      one workgroup per group on its slice
+//   lpt_assign_wave_kernel one wavefront per group of at most 64 workers on
+//                          its slice: one lane per worker, the greedy minimum
+//                          of key = load << 6 | lane by a DPP reduction per
+//                          tile, no LDS and no barrier (a group whose total
+//                          cost could overflow the 26-bit load is flagged)
+//   lpt_assign_kernel      one workgroup per group on its slice (larger or
+//                          flagged groups)
 //   worker_offsets_kernel  list offsets from the per-worker counts
 #include "device_util.h"
 #include "internal.h"
@@ -67,12 +73,13 @@ struct SchedWs {
   int32_t* gseq;           // two-level: LPT order split by group
   int32_t* wcount;         // two-level: tiles per worker [kMaxWorkers]
   int32_t* goff;           // two-level: start of each group's slice [kMaxGroups + 1]
+  int32_t* gslow;          // two-level: 1 = group left to lpt_assign_kernel [kMaxGroups]
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kMaxGroups = 64;
-constexpr size_t kSmallSlab = (kMaxWorkers + kMaxGroups + 1) * sizeof(int32_t);
+constexpr size_t kSmallSlab = (kMaxWorkers + 2 * kMaxGroups + 1) * sizeof(int32_t);
 
 SchedWs carve(void* ws, int tiles) {
   const size_t one = align_up(sizeof(int32_t) * (size_t)tiles, 256);
@@ -80,7 +87,7 @@ SchedWs carve(void* ws, int tiles) {
   auto at = [&](size_t i) { return reinterpret_cast<int32_t*>(b + i * one); };
   int32_t* small = at(10);
   return SchedWs{at(0), at(1), at(2), at(3), at(4), at(5), at(6), at(7), at(8), at(9),
-                 small, small + kMaxWorkers};
+                 small, small + kMaxWorkers, small + kMaxWorkers + kMaxGroups + 1};
 }
 
 __device__ inline int clamp_cost(int c) { return min(max(c, 0), kMaxCost); }
@@ -183,8 +190,10 @@ constexpr int kWorkerBits = 11;
 __global__ __launch_bounds__(kAssignThreads) void lpt_assign_kernel(
     const int32_t* __restrict__ cost, const int32_t* __restrict__ seq_all,
     int tiles_all, int n_workers_all, const int32_t* __restrict__ goff, int n_groups,
-    SchedWs ws, int32_t* __restrict__ worker_offsets, int64_t* __restrict__ worker_load) {
+    const int32_t* __restrict__ gslow, SchedWs ws, int32_t* __restrict__ worker_offsets,
+    int64_t* __restrict__ worker_load) {
   const int grp = blockIdx.x;
+  if (gslow && gslow[grp] == 0) return;      // done by lpt_assign_wave_kernel
   const int base_pos = goff ? goff[grp] : 0;
   const int tiles = goff ? goff[grp + 1] - base_pos : tiles_all;
   const int32_t* lpt_order = seq_all + base_pos;
@@ -463,6 +472,84 @@ __global__ __launch_bounds__(256) void lpt_scatter_kernel(
   if (k < tiles) worker_tiles[worker_offsets[ws.owner[k]] + ws.slot[k]] = lpt_order[k];
 }
 
+// Unsigned minimum over the wavefront, returned to every lane: an inclusive
+// scan inside each row of 16 lanes (row shifts 1, 2, 4, 8), then the row
+// results carried across rows (broadcast of lane 15 to rows 1 and 3, of lane
+// 31 to rows 2 and 3), so lane 63 holds the minimum of all 64.  Lanes whose
+// DPP source lies outside the row keep the identity 0xffffffff.
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+  constexpr int kId = -1;
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x111, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x112, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x114, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x118, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x142, 0xa, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+constexpr int kLaneBits = 6;                                  // lane index in a key
+constexpr int64_t kWaveLoadLimit = (int64_t(1) << (32 - kLaneBits)) - 1;
+
+// The greedy of lpt_assign_kernel for one group of at most 64 workers, one
+// tile at a time: worker j of the group is lane j, and the least-loaded
+// worker, lowest index on ties, is the minimum of load << 6 | j.  Same
+// owners, list positions, counts and loads as lpt_assign_kernel.
+__global__ __launch_bounds__(kWave) void lpt_assign_wave_kernel(
+    const int32_t* __restrict__ cost, const int32_t* __restrict__ seq_all, int n_workers_all,
+    const int32_t* __restrict__ goff, int n_groups, SchedWs ws,
+    int64_t* __restrict__ worker_load) {
+  const int grp = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int base_pos = goff[grp];
+  const int tiles = goff[grp + 1] - base_pos;
+  const int32_t* order = seq_all + base_pos;
+  const int nw = (n_workers_all - grp + n_groups - 1) / n_groups;
+  // every load stays below the group's total cost
+  long long total = 0;
+  for (int t = lane; t < tiles; t += kWave) total += clamp_cost(cost[order[t]]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) total += __shfl_xor(total, o);
+  if (total >= kWaveLoadLimit) {
+    if (lane == 0) ws.gslow[grp] = 1;
+    return;
+  }
+  if (lane == 0) ws.gslow[grp] = 0;
+  uint32_t key = lane < nw ? (uint32_t)lane : 0xffffffffu;
+  int32_t cnt = 0;
+  int32_t* owner = ws.owner + base_pos;
+  int32_t* slotp = ws.slot + base_pos;
+  for (int k = 0; k < tiles; k += kWave) {
+    const int t = k + lane;
+    const int32_t mine = t < tiles ? clamp_cost(cost[order[t]]) : 0;
+    int32_t my_owner = 0, my_slot = 0;
+    const int m = min(kWave, tiles - k);
+    for (int i = 0; i < m; ++i) {
+      const uint32_t c = (uint32_t)__builtin_amdgcn_readlane(mine, i);
+      const uint32_t kmin = wave_min_u32(key);
+      const int w = (int)(kmin & (kWave - 1));
+      const int32_t s = __builtin_amdgcn_readlane(cnt, w);
+      if (lane == w) {
+        cnt = s + 1;
+        key = kmin + (c << kLaneBits);
+      }
+      if (lane == i) {
+        my_owner = grp + w * n_groups;
+        my_slot = s;
+      }
+    }
+    if (t < tiles) {
+      owner[t] = my_owner;
+      slotp[t] = my_slot;
+      ws.owner_by_tile[order[t]] = my_owner;
+    }
+  }
+  if (lane < nw) {
+    worker_load[grp + lane * n_groups] = (int64_t)(key >> kLaneBits);
+    ws.wcount[grp + lane * n_groups] = cnt;
+  }
+}
+
 }  // namespace
 
 size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers) {
@@ -506,15 +593,22 @@ hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, in
     }
     hipLaunchKernelGGL(group_partition_kernel, dim3(1), dim3(kPartThreads), 0, s, lpt_order,
                        tiles, per_head, ws.head_group, X, ws.gseq, ws.goff);
+    // groups of at most one wavefront of workers take the one-wavefront
+    // greedy; lpt_assign_kernel then runs only the groups it flags
+    const bool wave = (n_workers + X - 1) / X <= kWave;
+    if (wave)
+      hipLaunchKernelGGL(lpt_assign_wave_kernel, dim3(X), dim3(kWave), 0, s, cost, ws.gseq,
+                         n_workers, ws.goff, X, ws, worker_load);
     hipLaunchKernelGGL(lpt_assign_kernel, dim3(X), dim3(kAssignThreads), 0, s, cost, ws.gseq,
-                       tiles, n_workers, ws.goff, X, ws, worker_offsets, worker_load);
+                       tiles, n_workers, ws.goff, X, wave ? ws.gslow : nullptr, ws,
+                       worker_offsets, worker_load);
     hipLaunchKernelGGL(worker_offsets_kernel, dim3(1), dim3(1024), 0, s, ws.wcount, n_workers,
                        worker_offsets);
     seq = ws.gseq;
   } else {
     hipLaunchKernelGGL(lpt_assign_kernel, dim3(1), dim3(kAssignThreads), 0, s, cost,
-                       lpt_order, tiles, n_workers, (const int32_t*)nullptr, 1, ws,
-                       worker_offsets, worker_load);
+                       lpt_order, tiles, n_workers, (const int32_t*)nullptr, 1,
+                       (const int32_t*)nullptr, ws, worker_offsets, worker_load);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
