@@ -220,6 +220,9 @@ SCHED_CASES = [
     ("random_odd", None, 100),
     ("big_costs", None, 256),
     ("max_heads", None, 256),        # the most heads the two-level schedule takes
+    # every head's load passes 2^26: groups holding one leave the one-wavefront
+    # assignment for the batch kernel, empty groups stay on the wavefront
+    ("huge_loads", None, 256),
 ]
 
 
@@ -243,6 +246,10 @@ def test_schedule_bit_exact(name, costs, W, tile_order, group, xg):
         costs = rng.integers(0, 16384, size=(5, 333))
     elif name == "max_heads":
         costs = rng.integers(0, 50, size=(4096, 3))
+    elif name == "huge_loads":
+        # pair tiles stay inside the 65535 cost clamp of the schedule ABI
+        costs = rng.integers(32000, 32768, size=(3, 2100))
+        assert costs.sum(1).min() >= 2 ** 26
     got = gpu_schedule(costs, W, tile_order, group, X)
     gc = olpt.group_costs(costs, group)
     if X > 1:
