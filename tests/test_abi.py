@@ -51,9 +51,10 @@ def test_workspace_sizes():
     rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert lib.fvattn_route_workspace_size(40, 75600, 128, 128) == 2 * rnd(pooled) + rnd(scores)
     assert lib.fvattn_route_workspace_size(0, 75600, 128, 128) == 0
-    # ten per-tile slabs plus counts/offsets for up to 2048 workers and 64 groups
+    # ten per-tile slabs plus per-worker counts (up to 2048 workers), group
+    # offsets (64 groups + 1) and per-group fallback flags (64 groups)
     assert lib.fvattn_schedule_workspace_size(40, 591, 256) == (
-        10 * rnd(40 * 591 * 4) + rnd((2048 + 65) * 4))
+        10 * rnd(40 * 591 * 4) + rnd((2048 + 2 * 64 + 1) * 4))
     assert lib.fvattn_schedule_workspace_size(40, 591, 0) == 0
     # SASA: row stats (float2) + 256-bin histograms + group state (16 B) +
     # per-row tie counts (int32) and offsets (int64)

@@ -181,3 +181,38 @@ def test_grouped_given_groups_tiles_stay_in_them(seed):
             assert hg[t // tph] == w % X
     assert sorted(tiles.tolist()) == list(range(H * tph))
     assert loads.sum() == costs.sum()
+
+
+# --- tile costs of q-block groups (the pair tiles of the persistent kernel) ---
+# A tile of `group` consecutive q-blocks of one head costs the kept blocks of
+# its q-blocks (the load unit is one sparse block: aixai.ru FVAttn post,
+# "Runtime Load Balancing (RLB)").  Worked by hand; nB = 5 is odd, so the last
+# pair tile of each head holds one q-block.
+_KV_HAND = np.array([[3, 1, 4, 1, 5],
+                     [9, 2, 6, 5, 3]])
+
+
+def test_group_costs_hand_example_odd_tail():
+    assert lpt.group_costs(_KV_HAND, 2).tolist() == [4, 5, 5, 11, 11, 3]
+    assert lpt.group_costs(_KV_HAND, 3).tolist() == [8, 6, 17, 8]
+    # one tile per head: the head's whole load
+    assert lpt.group_costs(_KV_HAND, 5).tolist() == [14, 25]
+    assert lpt.group_costs(_KV_HAND, 9).tolist() == [14, 25]
+
+
+def test_group_costs_one_is_identity():
+    rng = np.random.default_rng(3)
+    kv = rng.integers(0, 50, size=(4, 7))
+    assert lpt.group_costs(kv, 1).tolist() == kv.reshape(-1).tolist()
+
+
+@pytest.mark.parametrize("nb,group", [(1, 2), (2, 2), (7, 2), (591, 2), (10, 3), (11, 4)])
+def test_group_costs_shape_and_conservation(nb, group):
+    rng = np.random.default_rng(nb * 10 + group)
+    kv = rng.integers(0, nb + 1, size=(3, nb))
+    c = lpt.group_costs(kv, group).reshape(3, -1)
+    assert c.shape == (3, -(-nb // group))
+    assert c.sum(axis=1).tolist() == kv.sum(axis=1).tolist()
+    # the last tile holds the nb % group tail (or a full group)
+    tail = nb - (c.shape[1] - 1) * group
+    assert c[:, -1].tolist() == kv[:, nb - tail:].sum(axis=1).tolist()
