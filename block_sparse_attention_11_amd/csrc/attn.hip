@@ -837,7 +837,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   // and the tile's ordinal in this workgroup's sequence
   struct Walk {
     int it, h, i0, ca, cb, pa, pb, u, ord;
-    bool ina, inb, first;
+    bool ina, inb;
   };
   auto list_at = [&](int h, int i, int p) {
     return min(max(ld_uniform(a.kv_index + ((size_t)h * nb + i) * nb + p), 0), nb - 1);
@@ -866,10 +866,19 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   // tiles left (with claim_groups = x > 1, only among the lists of its own
   // group, w % x, so the groups stay independent like ranks); every hand-out
   // is one atomic add, so each tile runs exactly once whichever workgroup
-  // runs it.  Wave 0 makes the claims, two tiles
-  // ahead, and posts the list positions in an LDS ring; the other waves read
-  // a slot at least one barrier after it was written.  Pairs with no kept
-  // block are written as zeros by wave 0 while claiming.
+  // runs it.  Wave 0 makes the claims and posts the list positions in an LDS
+  // ring of four slots; pairs with no kept block are written as zeros by
+  // wave 0 while claiming.
+  //
+  // Ring order.  Tile ordinal k is opened (its slot read, by every wave)
+  // before the barrier of the step that runs the last union block of tile
+  // k-1.  Slots 0-2 are written before the start-up barrier; the slot of
+  // tile k+2 is written by wave 0 after the barrier of the step t that opens
+  // tile k.  Tile k+1 takes at least step t+1, so tile k+2 is opened at step
+  // t+2 or later, after barrier t+1, which wave 0 reaches only after its
+  // write: the read sees it even when every tile has a single union block.
+  // The slot's previous value (tile k-2) was read at a step no later than
+  // t-2, before that step's barrier, so the write cannot overtake the read.
   __shared__ int mbox[4];
   bool own_done = false;
   const int end_own = PERSIST ? ld_uniform(a.worker_offsets + blockIdx.x + 1) : end;
@@ -952,9 +961,11 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
     if (wave == 0) {
       const int c0 = claim();
       const int c1 = claim();
+      const int c2 = claim();
       if (lane == 0) {
         mbox[0] = c0;
         mbox[1] = c1;
+        mbox[2] = c2;
       }
     }
     lds_barrier();
@@ -966,7 +977,6 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
     if (dyn) {
       const int pos = __builtin_amdgcn_readfirstlane(mbox[ntile & 3]);
       w.ord = ntile++;
-      w.first = true;
       if (pos < 0) {
         w.it = end;
         return;
@@ -988,7 +998,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
       const int cb = i0 + 1 < nb ? min(ld_uniform(a.kv_count + (size_t)h * nb + i0 + 1), nb) : 0;
       if (ca > 0 || cb > 0) {
         w.it = it; w.h = h; w.i0 = i0; w.ca = ca; w.cb = cb; w.pa = 0; w.pb = 0;
-        w.ord = 0; w.first = true;
+        w.ord = 0;
         set_block(w);
         return;
       }
@@ -1000,7 +1010,6 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   auto advance = [&](Walk w) {
     w.pa += w.ina;
     w.pb += w.inb;
-    w.first = false;
     if (w.pa >= w.ca && w.pb >= w.cb) open_tile(w, w.it + 1);
     else set_block(w);
     return w;
@@ -1058,10 +1067,10 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
     // they fill were released by the barrier above)
     const bool mine = grp == 0 ? cur.ina : cur.inb;
     if (!mine && nxt.it < end) dma(kn, vn, nxt.h, nxt.u);
-    if (dyn && cur.first && wave == 0) {
-      // the tile two ahead of this one; its slot was last read two tiles ago
+    if (dyn && nxt.it != cur.it && nxt.it < end && wave == 0) {
+      // this step opened tile nxt.ord: post the tile two after it (ring order)
       const int c = claim();
-      if (lane == 0) mbox[(cur.ord + 2) & 3] = c;
+      if (lane == 0) mbox[(nxt.ord + 2) & 3] = c;
     }
     if (mine) {
       // the block in halves of HK keys: an online-softmax step per half keeps

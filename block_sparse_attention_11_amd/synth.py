@@ -74,6 +74,10 @@ WORKLOADS = {
     "long720p": Workload("long720p", 40, 128, (41, 45, 80), 128, 0.95, 8, "bf16",
                          note="40 heads, d=128, 41x45x80 tokens, block 128,"
                               " bf16; 4 steps with s_h redrawn per step"),
+    # The same long workload at Top-p 0.90 (the pages run both 0.95 and 0.90).
+    "long720p_p90": Workload("long720p_p90", 40, 128, (41, 45, 80), 128, 0.90, 8, "bf16",
+                             note="40 heads, d=128, 41x45x80 tokens, block 128,"
+                                  " bf16, Top-p 0.90; 4 steps with s_h redrawn per step"),
     # Supplementary, labelled: stronger Q/K coupling so routing is really sparse.
     # Routed density per head at this shape (Hilbert blocks, p = 0.95, k = 8):
     # s = 64 -> 0.89-0.92, s = 128 -> 0.54-0.88, s = 256 -> 0.02-0.58,

@@ -15,7 +15,8 @@ import torch
 
 from block_sparse_attention_11_amd import synth
 from block_sparse_attention_11_amd.pipeline import FVAttnPath
-from tests.test_gpu_fullsize import check_attention, check_route, check_schedule
+from tests.test_gpu_fullsize import (check_attention, check_gather, check_route,
+                                     check_schedule)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +49,8 @@ def test_degenerate_path(name):
     out = path.run(q, k, v, w.p, w.k)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    check_route(path, w, w.p, range(w.heads))
+    check_gather(path, q, k, range(w.heads))
+    check_route(path, w, w.p, range(w.heads), q, k)
     check_schedule(path)
     kvc = path.kv_count.cpu().numpy()
     nb = path.nb
@@ -57,7 +59,7 @@ def test_degenerate_path(name):
     if w.p < 1e-3 and w.k == 0:
         assert (kvc == 1).all()
     tiles = [(h, i) for h in range(w.heads) for i in range(nb)]
-    check_attention(path, w, v, out, tiles)
+    check_attention(path, w, q, k, v, out, tiles)
     # a second run on the same path object gives the same bytes
     out2 = path.run(q, k, v, w.p, w.k)
     torch.cuda.synchronize()
@@ -84,8 +86,9 @@ def test_every_mfma_shape(name, w, ranks):
     path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, device=DEV, **kw)
     out = path.run(q, k, v, w.p, w.k)
     torch.cuda.synchronize()
-    check_route(path, w, w.p, range(w.heads))
+    check_gather(path, q, k, range(w.heads))
+    check_route(path, w, w.p, range(w.heads), q, k)
     if not ranks:
         check_schedule(path)
     tiles = [(h, i) for h in range(w.heads) for i in range(path.nb)]
-    check_attention(path, w, v, out, tiles)
+    check_attention(path, w, q, k, v, out, tiles)

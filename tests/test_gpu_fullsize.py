@@ -59,15 +59,33 @@ def sample_tiles(path, n_random=6, seed=7):
     return sorted(picks)
 
 
-def check_route(path, w, p, heads):
-    """Every row of the given heads against the oracle's routing of the GPU's
-    Hilbert-ordered bytes; invariants on every head."""
+def oracle_rows(x, h, perm):
+    """Head h of x (token order) in the oracle's Hilbert order, float64 [1, n, d]."""
+    return ort.permute_rows(head_f64(x, h)[None], perm)
+
+
+def check_gather(path, q, k, heads):
+    """The GPU's Hilbert-ordered Q and K of the given heads equal, byte for
+    byte, the oracle's permutation of the original rows."""
+    perm, _ = ohb.hilbert_order(*path.grid)
+    bits = torch.int16 if q.dtype == torch.bfloat16 else torch.int32
+    for h in heads:
+        for src, got in ((q, path.qh), (k, path.kh)):
+            want = ort.permute_rows(src[h:h + 1].cpu().view(bits).numpy(), perm)
+            assert np.array_equal(got[h:h + 1].cpu().view(bits).numpy(), want), h
+    say(f"  Q/K gather bytes equal the oracle's on heads {list(heads)}")
+
+
+def check_route(path, w, p, heads, q, k):
+    """Every row of the given heads against the oracle's routing of the
+    original Q/K in the oracle's Hilbert order; invariants on every head."""
     nb = path.nb
+    perm, _ = ohb.hilbert_order(*w.grid)
     gc = path.kv_count.cpu().numpy()
     gi = path.kv_index.cpu().numpy()
     total = {"rows": 0, "exact": 0, "count": 0, "order": 0, "unexplained": 0}
     for h in heads:
-        ora = ort.route(head_f64(path.qh, h)[None], head_f64(path.kh, h)[None], w.block, p, w.k)
+        ora = ort.route(oracle_rows(q, h, perm), oracle_rows(k, h, perm), w.block, p, w.k)
         stats, bad = classify_rows(ora["P"], p, w.k, gc[h:h + 1], gi[h:h + 1],
                                    ora["kv_count"], ora["kv_index"])
         for key in total:
@@ -99,14 +117,15 @@ def check_schedule(path):
         assert np.array_equal(g.cpu().numpy(), r), what
 
 
-def check_attention(path, w, v, out, tiles):
-    perm = path.perm.cpu().numpy()
+def check_attention(path, w, q, k, v, out, tiles):
+    """Sampled tiles against the oracle on the original Q/K/V in the oracle's
+    Hilbert order, with the GPU's kept lists."""
+    perm, _ = ohb.hilbert_order(*w.grid)
     gc = path.kv_count.cpu().numpy()
     gi = path.kv_index.cpu().numpy()
     worst = {"max_abs": 0.0, "rel_l2": 0.0}
     for h in sorted({t[0] for t in tiles}):
-        qh, kh = head_f64(path.qh, h)[None], head_f64(path.kh, h)[None]
-        vh = ort.permute_rows(head_f64(v, h)[None], perm)
+        qh, kh, vh = (oracle_rows(x, h, perm) for x in (q, k, v))
         outh = out[h].float().cpu().numpy()
         ohh = outh[perm]                    # Hilbert order
         for (hh, i) in tiles:
@@ -135,9 +154,10 @@ def test_fullsize_path(name):
     assert np.array_equal(path.inv_perm.cpu().numpy(), inv)
     H = w.heads
     heads = sorted({0, 1, H // 2, H - 1} | ({32, 39} if H == 40 else set()))
-    check_route(path, w, p, heads)
+    check_gather(path, q, k, heads)
+    check_route(path, w, p, heads, q, k)
     check_schedule(path)
-    check_attention(path, w, v, out, sample_tiles(path))
+    check_attention(path, w, q, k, v, out, sample_tiles(path))
 
 
 def test_fullsize_480p_dense_control():
@@ -149,28 +169,31 @@ def test_fullsize_480p_dense_control():
     assert (gc == path.nb).all()
     assert (path.head_density.cpu().numpy() == 1.0).all()
     check_schedule(path)
-    check_attention(path, w, v, out, sample_tiles(path, n_random=4))
+    check_attention(path, w, q, k, v, out, sample_tiles(path, n_random=4))
 
 
-def test_fullsize_long720p_steps():
+@pytest.mark.parametrize("name", ["long720p", "long720p_p90"])
+def test_fullsize_long720p_steps(name):
     """Four steps of the long workload, s/K/E/V redrawn per step: routing,
     schedule and attention on fresh masks each step (all from one path
-    object, as a sampler would run it)."""
-    w = synth.WORKLOADS["long720p"]
+    object, as a sampler would run it), at Top-p 0.95 and 0.90."""
+    w = synth.WORKLOADS[name]
     path = FVAttnPath(w.heads, w.grid, w.d, w.block, device=DEV)
     perm, _ = ohb.hilbert_order(*w.grid)
     prev = None
     for step, r0 in synth.long_steps(w):
-        say(f"long720p step {step}")
+        say(f"{name} step {step} (p = {w.p})")
         ws = w.with_(seed=step)
         q, k, v, _ = synth.make_inputs(ws, DEV, r_override=r0)
         out = path.run(q, k, v, w.p, w.k)
         torch.cuda.synchronize()
         if step == 0:
             assert np.array_equal(path.perm.cpu().numpy(), perm)
-        check_route(path, w, w.p, [step, 39 - step])
+        heads = [step, 39 - step]
+        check_gather(path, q, k, heads)
+        check_route(path, w, w.p, heads, q, k)
         check_schedule(path)
-        check_attention(path, w, v, out, sample_tiles(path, n_random=3, seed=step))
+        check_attention(path, w, q, k, v, out, sample_tiles(path, n_random=3, seed=step))
         dens = path.head_density.cpu().numpy()
         if prev is not None:
             say(f"  density change vs previous step: max {np.abs(dens - prev).max():.4f}")
