@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 LIB_PATH = os.path.join(PKG, "libfvattn.so")
 HEADER = os.path.join(ROOT, "include", "fvattn.h")
 
-OK, EINVAL, EUNSUPPORTED, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4
+OK, EINVAL, EUNSUPPORTED, ELAUNCH, EWORKSPACE, ESCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 8 << 20
 F32, BF16 = 0, 1
 SCHED_TILE_ORDER = 1
 
@@ -59,6 +60,9 @@ _SIGNATURES = {
                                  _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _c_size_t, _c_void_p]),
+    "fvattn_schedule_noalloc": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p]),
     "fvattn_attn_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                      ctypes.POINTER(_c_int)]),
     "fvattn_sparse_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -268,6 +272,27 @@ def schedule(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
         _ptr(lpt_order), _ptr(worker_offsets),
         _ptr(worker_tiles), _ptr(worker_load), _ptr(workspace), ws_bytes,
         _stream(kv_count)))
+
+
+def schedule_noalloc(kv_count, n_workers: int, lpt_order, worker_offsets, worker_tiles,
+                     worker_load, tile_order: bool = False, group: int = 1,
+                     worker_groups: int = 1):
+    """schedule() with the library's static device scratch instead of a
+    workspace (for callers that cannot allocate); same outputs."""
+    _dev(kv_count, lpt_order, worker_offsets, worker_tiles, worker_load)
+    _need(kv_count.dim() == 2 and kv_count.dtype == torch.int32, "kv_count i32[H, nB]")
+    H, nb = kv_count.shape
+    tiles = H * ((nb + group - 1) // group)
+    _need(lpt_order.numel() == tiles and worker_tiles.numel() == tiles, "tile arrays")
+    _need(worker_offsets.numel() == n_workers + 1, "worker_offsets[W+1]")
+    _need(worker_load.numel() == n_workers and worker_load.dtype == torch.int64,
+          "worker_load i64[W]")
+    _check("fvattn_schedule_noalloc", load_library().fvattn_schedule_noalloc(
+        _ptr(kv_count), H, nb, int(group), int(n_workers),
+        (SCHED_TILE_ORDER if tile_order else 0)
+        | (SCHED_GROUPS(worker_groups) if worker_groups > 1 else 0),
+        _ptr(lpt_order), _ptr(worker_offsets),
+        _ptr(worker_tiles), _ptr(worker_load), _stream(kv_count)))
 
 
 def sparse_attn(q, k, v, o, block: int, kv_count, kv_index, worker_offsets=None,

@@ -31,6 +31,7 @@ const char* fvattn_status_string(int status) {
     case FVATTN_EUNSUPPORTED: return "unsupported configuration";
     case FVATTN_ELAUNCH: return "kernel launch failed";
     case FVATTN_EWORKSPACE: return "workspace missing or too small";
+    case FVATTN_ESCRATCH: return "problem larger than the static scratch of the no-allocation call";
     default: return "unknown status";
   }
 }
@@ -152,6 +153,35 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group
       kv_count, heads, n_qblocks, group, n_workers, n_groups > 1 ? n_groups : 1,
       (flags & FVATTN_SCHED_TILE_ORDER) != 0, nullptr,
       lpt_order, worker_offsets, worker_tiles, worker_load, workspace, stream));
+}
+
+int fvattn_schedule_noalloc(const int32_t* kv_count, int heads, int n_qblocks, int group,
+                            int n_workers, int flags, int32_t* lpt_order,
+                            int32_t* worker_offsets, int32_t* worker_tiles,
+                            int64_t* worker_load, hipStream_t stream) {
+  static_assert(fvattn::kNoAllocScratchBytes == FVATTN_NOALLOC_SCRATCH_BYTES, "scratch size");
+  if (!kv_count || !lpt_order || !worker_offsets || !worker_tiles || !worker_load)
+    return FVATTN_EINVAL;
+  if (heads < 1 || n_qblocks < 1 || n_workers < 1) return FVATTN_EINVAL;
+  if (group != 1 && group != 2) return FVATTN_EINVAL;
+  if (!fits_int32((long long)heads * n_qblocks)) return FVATTN_EINVAL;
+  if (flags & ~(FVATTN_SCHED_TILE_ORDER | FVATTN_SCHED_GROUPS(0xFF))) return FVATTN_EINVAL;
+  if (n_workers > fvattn::kMaxWorkers) return FVATTN_EUNSUPPORTED;
+  const int n_groups = (flags >> 8) & 0xFF;
+  if (n_groups > 1) {
+    if (n_groups > fvattn::schedule_max_groups() || n_groups > n_workers) return FVATTN_EINVAL;
+    if (heads > fvattn::schedule_max_group_heads()) return FVATTN_EUNSUPPORTED;
+  }
+  // the size check comes before any HIP call, so it holds without a device
+  if (fvattn::schedule_workspace_bytes(heads, n_qblocks, n_workers) >
+      fvattn::kNoAllocScratchBytes)
+    return FVATTN_ESCRATCH;
+  void* ws = nullptr;
+  if (fvattn::schedule_noalloc_scratch(&ws) != hipSuccess) return FVATTN_ELAUNCH;
+  return launch_status(fvattn::launch_schedule(
+      kv_count, heads, n_qblocks, group, n_workers, n_groups > 1 ? n_groups : 1,
+      (flags & FVATTN_SCHED_TILE_ORDER) != 0, nullptr,
+      lpt_order, worker_offsets, worker_tiles, worker_load, ws, stream));
 }
 
 int fvattn_schedule_heads(const int32_t* kv_count, int heads, int n_qblocks, int group,

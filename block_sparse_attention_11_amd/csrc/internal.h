@@ -78,6 +78,11 @@ hipError_t launch_schedule(const int32_t* kv_count, int heads, int n_qblocks, in
                            int64_t* worker_load, void* ws, hipStream_t s);
 int schedule_max_groups();
 int schedule_max_group_heads();
+// the no-allocation schedule's scratch: a static device array of
+// kNoAllocScratchBytes (FVATTN_NOALLOC_SCRATCH_BYTES); *ptr = its device
+// address on the current device (looked up once per device, thread-safe)
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+hipError_t schedule_noalloc_scratch(void** ptr);
 
 // ---- attn.hip --------------------------------------------------------------
 struct AttnArgs {

@@ -50,8 +50,18 @@
 //   lpt_assign_kernel      one workgroup per group on its slice (larger or
 //                          flagged groups)
 //   worker_offsets_kernel  list offsets from the per-worker counts
+#include <mutex>
+#include <unordered_map>
+
 #include "device_util.h"
 #include "internal.h"
+
+// Scratch of fvattn_schedule_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host the name is only a
+// stand-in for the symbol); it takes the device address from
+// hipGetSymbolAddress once per device and passes that.
+static __device__ __align__(256) unsigned char scratch[fvattn::kNoAllocScratchBytes];
 
 namespace fvattn {
 namespace {
@@ -556,6 +566,25 @@ size_t schedule_workspace_bytes(int heads, int n_qblocks, int n_workers) {
   (void)n_workers;
   const size_t tiles = (size_t)heads * n_qblocks;
   return 10 * align_up(sizeof(int32_t) * tiles, 256) + align_up(kSmallSlab, 256);
+}
+
+hipError_t schedule_noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::unordered_map<int, void*> by_device;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = by_device.find(dev);
+  if (it == by_device.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    it = by_device.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
 }
 
 int schedule_max_groups() { return kMaxGroups; }

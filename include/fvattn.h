@@ -21,8 +21,10 @@
  *    accumulation).
  *  - Ownership: the caller allocates every buffer (outputs and workspace) and
  *    keeps it alive until the stream work is done.  The library never
- *    allocates, frees or caches device memory and keeps no global state; it
- *    is re-entrant.
+ *    allocates, frees or caches device memory; it is re-entrant.  The one
+ *    piece of global state is the static scratch array of
+ *    fvattn_schedule_noalloc (one per GPU, for callers that cannot
+ *    allocate).
  *  - Streams: every call only enqueues kernels on `stream` (0 = the null
  *    stream) and returns; it never synchronises the host.
  *  - Errors: arguments are validated on the host before anything is
@@ -48,6 +50,8 @@ extern "C" {
 #define FVATTN_EUNSUPPORTED (-2) /* valid, but no kernel instance for it     */
 #define FVATTN_ELAUNCH (-3)      /* the HIP launch itself failed             */
 #define FVATTN_EWORKSPACE (-4)   /* workspace pointer null or too small      */
+#define FVATTN_ESCRATCH (-5)     /* larger than the static scratch of the
+                                    no-allocation call                       */
 
 /* Storage types. */
 #define FVATTN_F32 0
@@ -239,6 +243,30 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks,
                     int32_t* worker_offsets, int32_t* worker_tiles,
                     int64_t* worker_load, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fvattn_schedule for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, outputs, limits and errors as fvattn_schedule, except that
+ * there is no workspace argument: the scratch is a static device array of
+ * FVATTN_NOALLOC_SCRATCH_BYTES (8 MiB) that each GPU the library runs on
+ * holds until the process ends.  Problems whose
+ * fvattn_schedule_workspace_size(heads, n_qblocks, n_workers) exceeds it
+ * return FVATTN_ESCRATCH before anything is launched (about 209k
+ * heads * n_qblocks; 40 heads x 4096 q-blocks fit).  The call allocates and
+ * frees nothing; the first call on a device looks up the array's device
+ * address (hipGetSymbolAddress), later calls reuse it.  Nothing in the
+ * scratch needs clearing between calls (every word a kernel reads was
+ * written earlier in the same call).  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (two streams, or two
+ * host threads) race and give undefined results; order them on one stream.
+ * Outputs equal fvattn_schedule's bit for bit.
+ */
+#define FVATTN_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int fvattn_schedule_noalloc(const int32_t* kv_count, int heads, int n_qblocks,
+                            int group, int n_workers, int flags, int32_t* lpt_order,
+                            int32_t* worker_offsets, int32_t* worker_tiles,
+                            int64_t* worker_load, hipStream_t stream);
 
 /*
  * Two-level LPT with the head -> group map given: as fvattn_schedule with

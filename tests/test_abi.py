@@ -24,7 +24,7 @@ def test_library_is_built_in_tree():
 def test_exports_every_declared_symbol():
     lib = _lib.load_library()
     declared = _lib.declared_symbols()
-    assert len(declared) == 17, declared
+    assert len(declared) == 18, declared
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
@@ -40,6 +40,8 @@ def test_version_and_status_strings():
     assert _lib.status_string(0) == "ok"
     assert _lib.status_string(-1) == "invalid argument"
     assert _lib.status_string(-4) == "workspace missing or too small"
+    assert _lib.status_string(-5) == (
+        "problem larger than the static scratch of the no-allocation call")
     assert _lib.status_string(7) == "unknown status"
 
 
@@ -56,6 +58,10 @@ def test_workspace_sizes():
     assert lib.fvattn_schedule_workspace_size(40, 591, 256) == (
         10 * rnd(40 * 591 * 4) + rnd((2048 + 2 * 64 + 1) * 4))
     assert lib.fvattn_schedule_workspace_size(40, 591, 0) == 0
+    # the no-allocation schedule's static scratch takes 40 heads x 4096 q-blocks
+    # and refuses 64 x 4096
+    assert lib.fvattn_schedule_workspace_size(40, 4096, 2048) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.fvattn_schedule_workspace_size(64, 4096, 2048) > _lib.NOALLOC_SCRATCH_BYTES
     # SASA: row stats (float2) + 256-bin histograms + group state (16 B) +
     # per-row tie counts (int32) and offsets (int64)
     rows = 40 * 591
@@ -122,6 +128,18 @@ def _validation_main():
         (lib.fvattn_schedule(P, 40, 591, 1, 256, 65 << 8, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule(P, 40, 591, 1, 4, 8 << 8, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule(P, 4097, 2, 1, 256, 8 << 8, P, P, P, P, P, 1 << 30, N), EUNS),
+        # schedule on the static scratch: same checks, then the 8 MiB limit
+        # (checked before any HIP call)
+        (lib.fvattn_schedule_noalloc(P, 40, 591, 1, 2049, 0, P, P, P, P, N), EUNS),
+        (lib.fvattn_schedule_noalloc(P, 40, 591, 1, 256, 2, P, P, P, P, N), EINVAL),
+        (lib.fvattn_schedule_noalloc(N, 40, 591, 1, 256, 0, P, P, P, P, N), EINVAL),
+        (lib.fvattn_schedule_noalloc(P, 40, 591, 3, 256, 0, P, P, P, P, N), EINVAL),
+        (lib.fvattn_schedule_noalloc(P, 40, 591, 1, 4, 8 << 8, P, P, P, P, N), EINVAL),
+        (lib.fvattn_schedule_noalloc(P, 4097, 2, 1, 256, 8 << 8, P, P, P, P, N), EUNS),
+        (lib.fvattn_schedule_noalloc(P, 64, 4096, 2, 256, 8 << 8, P, P, P, P, N),
+         _lib.ESCRATCH),
+        (lib.fvattn_schedule_noalloc(P, 1, 1 << 30, 1, 256, 0, P, P, P, P, N),
+         _lib.ESCRATCH),
         # attention
         (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
