@@ -55,8 +55,8 @@ def attn_kernel_name(path) -> str:
     mfma = path.dtype == torch.bfloat16 and path.d in (64, 128) and path.block in (64, 128)
     if not mfma:
         return f"attn_simple_kernel<{path.d},persistent>"
-    if path.v_tiles and path.group == 2:
-        return f"attn_mfma_pair_kernel<{path.d},{path.block},persistent>"
+    if path.v_tiles and path.group in (2, 3):
+        return f"attn_mfma_tile_kernel<{path.d},{path.block},G={path.group},persistent>"
     if path.v_tiles:
         return f"attn_mfma_dma_kernel<{path.d},{path.block},persistent>"
     return f"attn_mfma_kernel<{path.d},{path.block},persistent>"
@@ -334,7 +334,7 @@ def main():
     ap.add_argument("--workload", default="720p", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--workers", type=int, default=0, help="persistent workgroups (0 = CUs)")
     ap.add_argument("--dense-steps", type=int, default=3)
-    ap.add_argument("--group", type=int, default=0, choices=(0, 1, 2),
+    ap.add_argument("--group", type=int, default=0, choices=(0, 1, 2, 3),
                     help="q-blocks per tile (0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-controls", action="store_true")

@@ -138,7 +138,7 @@ int fvattn_schedule(const int32_t* kv_count, int heads, int n_qblocks, int group
   if (!kv_count || !lpt_order || !worker_offsets || !worker_tiles || !worker_load)
     return FVATTN_EINVAL;
   if (heads < 1 || n_qblocks < 1 || n_workers < 1) return FVATTN_EINVAL;
-  if (group != 1 && group != 2) return FVATTN_EINVAL;
+  if (group < 1 || group > 3) return FVATTN_EINVAL;
   if (!fits_int32((long long)heads * n_qblocks)) return FVATTN_EINVAL;
   if (flags & ~(FVATTN_SCHED_TILE_ORDER | FVATTN_SCHED_GROUPS(0xFF))) return FVATTN_EINVAL;
   if (n_workers > fvattn::kMaxWorkers) return FVATTN_EUNSUPPORTED;
@@ -163,7 +163,7 @@ int fvattn_schedule_noalloc(const int32_t* kv_count, int heads, int n_qblocks, i
   if (!kv_count || !lpt_order || !worker_offsets || !worker_tiles || !worker_load)
     return FVATTN_EINVAL;
   if (heads < 1 || n_qblocks < 1 || n_workers < 1) return FVATTN_EINVAL;
-  if (group != 1 && group != 2) return FVATTN_EINVAL;
+  if (group < 1 || group > 3) return FVATTN_EINVAL;
   if (!fits_int32((long long)heads * n_qblocks)) return FVATTN_EINVAL;
   if (flags & ~(FVATTN_SCHED_TILE_ORDER | FVATTN_SCHED_GROUPS(0xFF))) return FVATTN_EINVAL;
   if (n_workers > fvattn::kMaxWorkers) return FVATTN_EUNSUPPORTED;
@@ -193,7 +193,7 @@ int fvattn_schedule_heads(const int32_t* kv_count, int heads, int n_qblocks, int
       !worker_load)
     return FVATTN_EINVAL;
   if (heads < 1 || n_qblocks < 1 || n_workers < 1) return FVATTN_EINVAL;
-  if (group != 1 && group != 2) return FVATTN_EINVAL;
+  if (group < 1 || group > 3) return FVATTN_EINVAL;
   if (!fits_int32((long long)heads * n_qblocks)) return FVATTN_EINVAL;
   if (flags & ~FVATTN_SCHED_TILE_ORDER) return FVATTN_EINVAL;
   if (n_groups < 2 || n_groups > fvattn::schedule_max_groups() || n_groups > n_workers)
@@ -263,7 +263,7 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   if (!dtype_ok(dtype) || heads < 1 || n < 1 || d < 1 || block < 1) return FVATTN_EINVAL;
   if (isnan(scale) || isinf(scale)) return FVATTN_EINVAL;
   if (v_layout != FVATTN_V_ROWS && v_layout != FVATTN_V_TILES) return FVATTN_EINVAL;
-  if (group != 1 && group != 2) return FVATTN_EINVAL;
+  if (group < 1 || group > 3) return FVATTN_EINVAL;
   if (!fits_int32((long long)n * d) || heads > 65535) return FVATTN_EINVAL;
   const int64_t nb = nblocks(n, block);
   if (!fits_int32((long long)heads * nb) || !fits_int32(nb * nb)) return FVATTN_EINVAL;
@@ -273,13 +273,18 @@ int fvattn_sparse_attn(const void* q, const void* k, const void* v, void* o, int
   const bool bf16 = dtype == FVATTN_BF16;
   if (!fvattn::attn_has_mfma_instance(bf16, d, block) && (d > 128 || block > 256))
     return FVATTN_EUNSUPPORTED;
-  // the tiled-V kernel addresses each tensor with one 32-bit buffer offset;
-  // tiles exist only for blocks of a multiple of 16 rows (fvattn_pack_v)
+  // the tiled-V kernels address one head of K and of V at a time with 32-bit
+  // byte offsets; tiles exist only for blocks of a multiple of 16 rows
+  // (fvattn_pack_v)
   if (v_layout == FVATTN_V_TILES &&
-      ((long long)heads * nb * block * d * 2 > 0x7fffffffLL || block % 16 != 0))
+      ((long long)nb * block * d * 2 > 0xffffffffLL || block % 16 != 0))
     return FVATTN_EUNSUPPORTED;
   if ((timing || claims) && !worker_offsets) return FVATTN_EINVAL;
   if (claim_groups < 0 || claim_groups > 64) return FVATTN_EINVAL;
+  // three q-blocks per tile: bf16 V tiles of 128-key blocks, d 64 or 128
+  if (group == 3 &&
+      !fvattn::attn_has_group3_instance(bf16, d, block, v_layout == FVATTN_V_TILES))
+    return FVATTN_EUNSUPPORTED;
   fvattn::AttnArgs a;
   a.q = q;
   a.k = k;
@@ -311,7 +316,10 @@ int fvattn_attn_workers(int dtype, int d, int block, int v_layout, int group,
                         int* workers) {
   if (!workers || !dtype_ok(dtype) || d < 1 || block < 1) return FVATTN_EINVAL;
   if (v_layout != FVATTN_V_ROWS && v_layout != FVATTN_V_TILES) return FVATTN_EINVAL;
-  if (group != 1 && group != 2) return FVATTN_EINVAL;
+  if (group < 1 || group > 3) return FVATTN_EINVAL;
+  if (group == 3 && !fvattn::attn_has_group3_instance(dtype == FVATTN_BF16, d, block,
+                                                      v_layout == FVATTN_V_TILES))
+    return FVATTN_EUNSUPPORTED;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FVATTN_ELAUNCH;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

@@ -487,6 +487,18 @@ __device__ inline uint32_t vt_off(int dd, int chunk) {
   return (uint32_t)(dd * (2 * BLK) + ((chunk ^ vt_swz<BLK>(dd)) << 4));
 }
 
+// Buffer descriptor over head h of a tensor whose heads lie head_bytes apart
+// (head_bytes < 2^32).  Loads through it take their whole byte offset in the
+// per-lane offset operand, which the hardware range check covers: offsets at
+// or past head_bytes read as zero, so the rows past the end of a head (the
+// short last block) never touch memory outside it, and no tensor size limit
+// comes from 32-bit offsets beyond the size of one head.
+__device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int h, uint32_t head_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(static_cast<const uint8_t*>(base) + (size_t)h * head_bytes), (short)0,
+      (int)head_bytes, 0x00020000);
+}
+
 // read-only table entry through the scalar cache (the tables are not written
 // while the kernel runs and the index is wave-uniform)
 __device__ inline int32_t ld_uniform(const int32_t* p) {
@@ -516,13 +528,10 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   uint16_t* O = static_cast<uint16_t*>(a.o);
   const float sl2 = a.scale_log2;
-  // one descriptor per tensor (the host checks both fit 32-bit offsets); K
-  // rows past the end of the tensor read as zero, rows past the end of a head
-  // read the next head's rows, which the score mask removes
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)a.k, (short)0, (int)((size_t)a.heads * n * D * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)a.v, (short)0, (int)((size_t)a.heads * nb * D * BLK * 2), 0x00020000);
+  // one descriptor per head (head_rsrc): K rows past the end of a head read
+  // as zero and the score mask removes them
+  const uint32_t kbytes = (uint32_t)((size_t)n * D * 2);
+  const uint32_t vbytes = (uint32_t)((size_t)nb * D * BLK * 2);
 
   // per-lane DMA source offsets inside one block (bytes), fixed for the kernel
   uint32_t koff[KDMA], voff[VDMA];
@@ -539,18 +548,20 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
     voff[x] = (uint32_t)(dd * BLK * 2 + (pc ^ vt_swz<BLK>(dd)) * 16);
   }
   auto dma_k = [&](int h, int j) {
-    const uint32_t base = (uint32_t)(((size_t)h * n + (size_t)j * BLK) * D * 2);
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k, h, kbytes);
+    const uint32_t base = (uint32_t)j * (BLK * D * 2);
 #pragma unroll
     for (int x = 0; x < KDMA; ++x)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          krs, (lds_void*)(Ks + (x * NW + wave) * 1024), 16, koff[x], base, 0, 0);
+          krs, (lds_void*)(Ks + (x * NW + wave) * 1024), 16, base + koff[x], 0, 0, 0);
   };
   auto dma_v = [&](int h, int j) {
-    const uint32_t base = (uint32_t)(((size_t)h * nb + j) * D * BLK * 2);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v, h, vbytes);
+    const uint32_t base = (uint32_t)j * (D * BLK * 2);
 #pragma unroll
     for (int x = 0; x < VDMA; ++x)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vrs, (lds_void*)(Vs + (x * NW + wave) * 1024), 16, voff[x], base, 0, 0);
+          vrs, (lds_void*)(Vs + (x * NW + wave) * 1024), 16, base + voff[x], 0, 0, 0);
   };
 
   uint64_t t0 = 0;
@@ -751,27 +762,40 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel for tiles of two q-blocks (group = 2), V as tiles.
+// bf16 MFMA kernel for tiles of G consecutive q-blocks (group = G = 2 or 3),
+// V as tiles.
 //
-// The kernel is bound by streaming K and V^T (64 KB per kept block pair at
-// d = 128), so one workgroup of 2*BLK/32 wavefronts serves two consecutive
-// q-blocks of a head and loads each key block once for both: it walks the
-// union of the two ascending kept lists, and each half of the workgroup
-// computes only on the blocks its own q-block kept.  K and V^T are double
+// Every kept (q-block, key block) pair streams a 64 KB K + V^T block (d =
+// 128) from L2 into LDS, so one workgroup of G*BLK/32 wavefronts serves G
+// consecutive q-blocks of a head and loads each key block once for all of
+// them: it walks the union of the G ascending kept lists, and the
+// wavefronts of each q-block compute only on the blocks their q-block kept
+// (BLK/32 wavefronts of 32 queries per q-block; wavefront w runs on SIMD
+// w % 4, so each SIMD holds one wavefront of every q-block).  K and V^T are double
 // buffered in four LDS arrays (the loop body is instantiated for both buffer
 // assignments, so the compiler sees distinct objects and does not wait on the
 // in-flight copy): the copy of union block u+1 is issued right after the one
-// barrier of block u and overlaps all of block u's work.
+// barrier of block u and overlaps all of block u's work.  HK is the key
+// width of one online-softmax step (the block is processed in BLK/HK steps).
 // ---------------------------------------------------------------------------
-template <int D, int BLK, bool PERSIST, bool CONFINED = false>
-__global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
+// The persistent launch (worker lists) and the head-major grid launch (one
+// workgroup per tile, worker_offsets == null) run this one compiled body, so
+// both give the same bits for a tile.
+template <int D, int BLK, int G, int HK, bool CONFINED = false>
+__global__ __launch_bounds__(2 * G * BLK) void attn_mfma_tile_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NW = 2 * BLK / 32;            // wavefronts, both q-blocks
+  const bool PERSIST = a.worker_offsets != nullptr;
+  constexpr int WPQ = BLK / 32;               // wavefronts per q-block
+  constexpr int NW = G * WPQ;                 // wavefronts, all q-blocks
   constexpr int CPRK = D / 8;
   constexpr int CPRV = BLK / 8;
-  constexpr int KDMA = BLK * CPRK / (64 * NW);
-  constexpr int VDMA = D * CPRV / (64 * NW);
-  static_assert(KDMA * 64 * NW == BLK * CPRK && VDMA * 64 * NW == D * CPRV, "DMA split");
+  // 1 KB DMA instructions per block (64 lanes x 16 bytes) and the most any
+  // wavefront issues: wavefront w takes instructions w, w + NW, ...
+  constexpr int NIK = BLK * CPRK / 64;
+  constexpr int NIV = D * CPRV / 64;
+  constexpr int KDMA = (NIK + NW - 1) / NW;
+  constexpr int VDMA = (NIV + NW - 1) / NW;
+  static_assert(G >= 2 && G <= 3 && BLK % HK == 0 && HK % 32 == 0, "tile shape");
   __shared__ __attribute__((aligned(1024))) uint8_t K0[BLK * D * 2];
   __shared__ __attribute__((aligned(1024))) uint8_t K1[BLK * D * 2];
   __shared__ __attribute__((aligned(1024))) uint8_t V0[D * BLK * 2];
@@ -780,22 +804,23 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int grp = wave / (NW / 2);            // which q-block of the pair
-  const int wq = wave % (NW / 2);             // 32-query slice inside it
+  const int grp = wave / WPQ;                 // which q-block of the tile
+  const int wq = wave % WPQ;                  // 32-query slice inside it
   const int col = lane & 31;
   const int g = lane >> 5;
   const int n = a.n, nb = a.nb, tph = a.tiles_per_head;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   uint16_t* O = static_cast<uint16_t*>(a.o);
   const float sl2 = a.scale_log2;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)a.k, (short)0, (int)((size_t)a.heads * n * D * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)a.v, (short)0, (int)((size_t)a.heads * nb * D * BLK * 2), 0x00020000);
+  // one descriptor per head (head_rsrc): K rows past the end of a head read
+  // as zero and the score mask removes them
+  const uint32_t kbytes = (uint32_t)((size_t)n * D * 2);
+  const uint32_t vbytes = (uint32_t)((size_t)nb * D * BLK * 2);
 
-  // DMA instruction x of this wave fills LDS chunks P = (x*NW + wave)*64 + lane;
-  // consecutive x advance by NW*64 chunks = a whole number of rows that is a
-  // multiple of the swizzle period, so the source offset is affine in x
+  // DMA instruction x of this wave fills LDS chunks P = (x*NW + wave)*64 + lane
+  // (when x*NW + wave is below the instruction count); consecutive x advance
+  // by NW*64 chunks = a whole number of rows that is a multiple of the
+  // swizzle period, so the source offset is affine in x
   static_assert((NW * 64 / CPRK) % CPRK == 0 && (NW * 64 / CPRV) % 16 == 0, "swizzle period");
   constexpr uint32_t kStepK = (NW * 64 / CPRK) * D * 2;     // bytes per DMA step, K
   constexpr uint32_t kStepV = (NW * 64 / CPRV) * BLK * 2;   // and V^T
@@ -808,16 +833,20 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
     voff = (uint32_t)(dd * BLK * 2 + (pv ^ vt_swz<BLK>(dd)) * 16);
   }
   auto dma = [&](uint8_t* kb, uint8_t* vb, int h, int j) {
-    const uint32_t kbase = (uint32_t)(((size_t)h * n + (size_t)j * BLK) * D * 2);
-    const uint32_t vbase = (uint32_t)(((size_t)h * nb + j) * D * BLK * 2);
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k, h, kbytes);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v, h, vbytes);
+    const uint32_t kbase = (uint32_t)j * (BLK * D * 2) + koff;
+    const uint32_t vbase = (uint32_t)j * (D * BLK * 2) + voff;
 #pragma unroll
     for (int x = 0; x < KDMA; ++x)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          krs, (lds_void*)(kb + (x * NW + wave) * 1024), 16, koff, kbase + x * kStepK, 0, 0);
+      if (NIK % NW == 0 || x * NW + wave < NIK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            krs, (lds_void*)(kb + (x * NW + wave) * 1024), 16, kbase + x * kStepK, 0, 0, 0);
 #pragma unroll
     for (int x = 0; x < VDMA; ++x)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vrs, (lds_void*)(vb + (x * NW + wave) * 1024), 16, voff, vbase + x * kStepV, 0, 0);
+      if (NIV % NW == 0 || x * NW + wave < NIV)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vrs, (lds_void*)(vb + (x * NW + wave) * 1024), 16, vbase + x * kStepV, 0, 0, 0);
   };
 
   uint64_t t0 = 0;
@@ -833,21 +862,30 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
   if (dyn) end = 0x7fffffff;
 
   // walk state (wave-uniform): position in the worker list (a position in
-  // worker_tiles), the pair, the two list cursors, the current union block,
-  // and the tile's ordinal in this workgroup's sequence
+  // worker_tiles), the tile's head and first q-block, the G list lengths and
+  // cursors, the current union block and which lists hold it (bit g), and
+  // the tile's ordinal in this workgroup's sequence
   struct Walk {
-    int it, h, i0, ca, cb, pa, pb, u, ord;
-    bool ina, inb;
+    int it, h, i0, c[G], p[G], u, ord, in;
   };
   auto list_at = [&](int h, int i, int p) {
     return min(max(ld_uniform(a.kv_index + ((size_t)h * nb + i) * nb + p), 0), nb - 1);
   };
   auto set_block = [&](Walk& w) {
-    const int ja = w.pa < w.ca ? list_at(w.h, w.i0, w.pa) : nb;
-    const int jb = w.pb < w.cb ? list_at(w.h, w.i0 + 1, w.pb) : nb;
-    w.u = min(ja, jb);
-    w.ina = ja == w.u;
-    w.inb = jb == w.u;
+    int jg[G];
+#pragma unroll
+    for (int g2 = 0; g2 < G; ++g2)
+      jg[g2] = w.p[g2] < w.c[g2] ? list_at(w.h, w.i0 + g2, w.p[g2]) : nb;
+    w.u = jg[0];
+#pragma unroll
+    for (int g2 = 1; g2 < G; ++g2) w.u = min(w.u, jg[g2]);
+    w.in = 0;
+#pragma unroll
+    for (int g2 = 0; g2 < G; ++g2) w.in |= (jg[g2] == w.u) << g2;
+  };
+  // kept count of q-block i0 + g2 of head h (0 past the last q-block)
+  auto count_at = [&](int h, int i0, int g2) {
+    return i0 + g2 < nb ? min(ld_uniform(a.kv_count + (size_t)h * nb + i0 + g2), nb) : 0;
   };
   auto zero_rows = [&](int h, int i) {
     const int qr = i * BLK + wq * 32 + col;
@@ -942,12 +980,13 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
       }
       const int tile = ld_uniform(a.worker_tiles + pos);
       const int h = tile / tph;
-      const int i0 = (tile - h * tph) * 2;
-      const int ca = ld_uniform(a.kv_count + (size_t)h * nb + i0);
-      const int cb = i0 + 1 < nb ? ld_uniform(a.kv_count + (size_t)h * nb + i0 + 1) : 0;
-      if (ca > 0 || cb > 0) return pos;
-      // nothing kept: zero both q-blocks' rows here
-      for (int r = lane; r < 2 * BLK; r += 64) {
+      const int i0 = (tile - h * tph) * G;
+      int any = 0;
+#pragma unroll
+      for (int g2 = 0; g2 < G; ++g2) any |= count_at(h, i0, g2);
+      if (any > 0) return pos;
+      // nothing kept: zero the tile's rows here
+      for (int r = lane; r < G * BLK; r += 64) {
         const int qr = i0 * BLK + r;
         if (qr < n) {
           u32x4* orow = reinterpret_cast<u32x4*>(O + ((size_t)h * n + out_row(a, qr)) * D);
@@ -983,21 +1022,30 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
       }
       const int tile = ld_uniform(a.worker_tiles + pos);
       const int h = tile / tph;
-      const int i0 = (tile - h * tph) * 2;
-      w.it = pos; w.h = h; w.i0 = i0; w.pa = 0; w.pb = 0;
-      w.ca = min(ld_uniform(a.kv_count + (size_t)h * nb + i0), nb);
-      w.cb = i0 + 1 < nb ? min(ld_uniform(a.kv_count + (size_t)h * nb + i0 + 1), nb) : 0;
+      const int i0 = (tile - h * tph) * G;
+      w.it = pos; w.h = h; w.i0 = i0;
+#pragma unroll
+      for (int g2 = 0; g2 < G; ++g2) {
+        w.c[g2] = count_at(h, i0, g2);
+        w.p[g2] = 0;
+      }
       set_block(w);
       return;
     }
     while (it < end) {
       const int tile = PERSIST ? ld_uniform(a.worker_tiles + it) : it;
       const int h = tile / tph;
-      const int i0 = (tile - h * tph) * 2;
-      const int ca = min(ld_uniform(a.kv_count + (size_t)h * nb + i0), nb);
-      const int cb = i0 + 1 < nb ? min(ld_uniform(a.kv_count + (size_t)h * nb + i0 + 1), nb) : 0;
-      if (ca > 0 || cb > 0) {
-        w.it = it; w.h = h; w.i0 = i0; w.ca = ca; w.cb = cb; w.pa = 0; w.pb = 0;
+      const int i0 = (tile - h * tph) * G;
+      int any = 0;
+#pragma unroll
+      for (int g2 = 0; g2 < G; ++g2) {
+        w.c[g2] = count_at(h, i0, g2);
+        any |= w.c[g2];
+      }
+      if (any > 0) {
+        w.it = it; w.h = h; w.i0 = i0;
+#pragma unroll
+        for (int g2 = 0; g2 < G; ++g2) w.p[g2] = 0;
         w.ord = 0;
         set_block(w);
         return;
@@ -1008,9 +1056,13 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
     w.it = end;
   };
   auto advance = [&](Walk w) {
-    w.pa += w.ina;
-    w.pb += w.inb;
-    if (w.pa >= w.ca && w.pb >= w.cb) open_tile(w, w.it + 1);
+    bool done = true;
+#pragma unroll
+    for (int g2 = 0; g2 < G; ++g2) {
+      w.p[g2] += (w.in >> g2) & 1;
+      done = done && w.p[g2] >= w.c[g2];
+    }
+    if (done) open_tile(w, w.it + 1);
     else set_block(w);
     return w;
   };
@@ -1065,7 +1117,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
     // issue their share now, the others after their first S product, so the
     // copies do not compete with the step's first LDS reads (the buffers
     // they fill were released by the barrier above)
-    const bool mine = grp == 0 ? cur.ina : cur.inb;
+    const bool mine = (cur.in >> grp) & 1;
     if (!mine && nxt.it < end) dma(kn, vn, nxt.h, nxt.u);
     if (dyn && nxt.it != cur.it && nxt.it < end && wave == 0) {
       // this step opened tile nxt.ord: post the tile two after it (ring order)
@@ -1073,10 +1125,9 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
       if (lane == 0) mbox[(nxt.ord + 2) & 3] = c;
     }
     if (mine) {
-      // the block in halves of HK keys: an online-softmax step per half keeps
-      // the live score / probability registers small
-      constexpr int HK = BLK >= 128 ? 64 : BLK;
-      constexpr int KT = HK / 32;              // 32-key tiles per half
+      // the block in steps of HK keys: an online-softmax step per HK keys
+      // keeps the live score / probability registers small
+      constexpr int KT = HK / 32;              // 32-key tiles per step
       const int j = cur.u;
       const int r0 = j * BLK;
 #pragma unroll
@@ -1100,9 +1151,8 @@ __global__ __launch_bounds__(4 * BLK) void attn_mfma_pair_kernel(AttnArgs a) {
           // the first half starts right after the barrier with nothing else
           // to overlap: keep kReadAhead K reads in flight ahead of the MFMAs
           // (the default schedule waits on every second read)
-          constexpr int kReadAhead = 6;
           constexpr int kN = (D / 16) * KT;
-          static_assert(kN > kReadAhead, "read-ahead depth");
+          constexpr int kReadAhead = kN > 6 ? 6 : kN - 1;
           __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);   // LDS reads
 #pragma unroll
           for (int x = 0; x < kN - kReadAhead; ++x) {
@@ -1201,21 +1251,31 @@ __global__ void claims_reset_kernel(int32_t* c, int n) {
   if (i < n) c[i] = 0;
 }
 
-template <int D, int BLK>
-hipError_t launch_mfma_pair(const AttnArgs& a, hipStream_t s) {
+// key width of one online-softmax step.  Every step pays a fixed cost (the
+// scores' MFMAs drain before the row max, the max exchange, the rescale
+// vote), so tiles of two q-blocks take the whole block in one step (231
+// VGPRs at d = block = 128, no spills); three q-blocks per tile (three
+// wavefronts per SIMD, at most 168 VGPRs each) take 32-key steps.
+template <int BLK, int G>
+constexpr int tile_hk() { return G == 2 ? BLK : 32; }
+
+template <int D, int BLK, int G>
+hipError_t launch_mfma_tile(const AttnArgs& a, hipStream_t s) {
+  constexpr int HK = tile_hk<BLK, G>();
+  constexpr int threads = 2 * G * BLK;
   if (a.worker_offsets && a.claims) {
     hipLaunchKernelGGL(claims_reset_kernel, dim3((a.n_workers + 255) / 256), dim3(256), 0, s,
                        a.claims, a.n_workers);
   }
   if (a.worker_offsets && a.claims && a.claim_groups > 1) {
-    hipLaunchKernelGGL((attn_mfma_pair_kernel<D, BLK, true, true>), dim3(a.n_workers),
-                       dim3(4 * BLK), 0, s, a);
+    hipLaunchKernelGGL((attn_mfma_tile_kernel<D, BLK, G, HK, true>), dim3(a.n_workers),
+                       dim3(threads), 0, s, a);
   } else if (a.worker_offsets) {
-    hipLaunchKernelGGL((attn_mfma_pair_kernel<D, BLK, true>), dim3(a.n_workers),
-                       dim3(4 * BLK), 0, s, a);
+    hipLaunchKernelGGL((attn_mfma_tile_kernel<D, BLK, G, HK>), dim3(a.n_workers),
+                       dim3(threads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((attn_mfma_pair_kernel<D, BLK, false>),
-                       dim3(a.heads * a.tiles_per_head), dim3(4 * BLK), 0, s, a);
+    hipLaunchKernelGGL((attn_mfma_tile_kernel<D, BLK, G, HK>),
+                       dim3(a.heads * a.tiles_per_head), dim3(threads), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -1280,7 +1340,12 @@ hipError_t attn_occupancy(bool bf16, int d, int block, bool v_tiles, int group,
 #define FV_OCC(D, B)                                                                          \
   if (d == D && block == B) {                                                                 \
     if (v_tiles && group == 2)                                                                \
-      return occupancy_of(attn_mfma_pair_kernel<D, B, true>, 2 * threads, per_cu);            \
+      return occupancy_of(attn_mfma_tile_kernel<D, B, 2, tile_hk<B, 2>()>, 2 * threads, \
+                          per_cu);                                                            \
+    if constexpr (B == 128)                                                                   \
+      if (v_tiles && group == 3)                                                              \
+        return occupancy_of(attn_mfma_tile_kernel<D, B, 3, tile_hk<B, 3>()>,            \
+                            3 * threads, per_cu);                                             \
     return v_tiles ? occupancy_of(attn_mfma_dma_kernel<D, B, true>, threads, per_cu)          \
                    : occupancy_of(attn_mfma_kernel<D, B, true>, threads, per_cu);             \
   }
@@ -1301,6 +1366,10 @@ hipError_t attn_occupancy(bool bf16, int d, int block, bool v_tiles, int group,
   return occupancy_of(attn_simple_kernel<float, 128, true>, kSimpleThreads, per_cu);
 }
 
+bool attn_has_group3_instance(bool bf16, int d, int block, bool v_tiles) {
+  return bf16 && v_tiles && block == 128 && (d == 64 || d == 128);
+}
+
 bool attn_has_mfma_instance(bool bf16, int d, int block) {
   if (!bf16) return false;
   return (d == 64 || d == 128) && (block == 64 || block == 128);
@@ -1308,10 +1377,16 @@ bool attn_has_mfma_instance(bool bf16, int d, int block) {
 
 hipError_t launch_sparse_attn(const AttnArgs& a, bool bf16, hipStream_t s) {
   if (attn_has_mfma_instance(bf16, a.d, a.block) && a.v_tiles && a.group == 2) {
-    if (a.d == 128 && a.block == 128) return launch_mfma_pair<128, 128>(a, s);
-    if (a.d == 64 && a.block == 64) return launch_mfma_pair<64, 64>(a, s);
-    if (a.d == 64 && a.block == 128) return launch_mfma_pair<64, 128>(a, s);
-    return launch_mfma_pair<128, 64>(a, s);
+    if (a.d == 128 && a.block == 128) return launch_mfma_tile<128, 128, 2>(a, s);
+    if (a.d == 64 && a.block == 64) return launch_mfma_tile<64, 64, 2>(a, s);
+    if (a.d == 64 && a.block == 128) return launch_mfma_tile<64, 128, 2>(a, s);
+    return launch_mfma_tile<128, 64, 2>(a, s);
+  }
+  if (a.group == 3) {
+    // three q-blocks per tile: 128-key blocks with V tiles only (the ABI
+    // refuses the rest)
+    if (a.d == 128) return launch_mfma_tile<128, 128, 3>(a, s);
+    return launch_mfma_tile<64, 128, 3>(a, s);
   }
   if (attn_has_mfma_instance(bf16, a.d, a.block) && a.v_tiles) {
     if (a.d == 128 && a.block == 128) return launch_mfma_dma<128, 128>(a, s);

@@ -106,6 +106,8 @@ struct AttnArgs {
   int tiles_per_head;             // ceil(nb / group)
 };
 bool attn_has_mfma_instance(bool bf16, int d, int block);
+// tiles of three q-blocks (group 3) run only on this instance set
+bool attn_has_group3_instance(bool bf16, int d, int block, bool v_tiles);
 // resident persistent workgroups per CU of the kernel that would run
 hipError_t attn_occupancy(bool bf16, int d, int block, bool v_tiles, int group,
                           int* per_cu);

@@ -69,7 +69,7 @@ class FVAttnPath:
         self._vh = (torch.empty((H, nb, d, block), dtype=dtype, device=dev) if self.v_tiles
                     else torch.empty_like(self.qh))
         self.oh = torch.empty_like(self.qh)
-        # tiles of two q-blocks share each K/V block load (tiled V only)
+        # tiles of two (or three) q-blocks share each K/V block load (tiled V only)
         self.group = (2 if self.v_tiles else 1) if group is None else group
         self.tiles = H * ((nb + self.group - 1) // self.group)
         with torch.cuda.device(dev):

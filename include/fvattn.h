@@ -193,10 +193,10 @@ int fvattn_route_pooled(const float* qbar, const float* kbar, int heads, int n, 
 
 /*
  * LPT work list over tiles for n_workers persistent workgroups.  A tile is
- * `group` consecutive q-blocks of one head (group 1 or 2): tile
+ * `group` consecutive q-blocks of one head (group 1, 2 or 3): tile
  * t = h * ceil(n_qblocks / group) + m covers q-blocks [m*group,
- * min(n_qblocks, (m+1)*group)).  group 2 matches the attention kernel that
- * loads each K/V block once for two q-blocks.
+ * min(n_qblocks, (m+1)*group)).  group 2 and 3 match the attention kernels
+ * that load each K/V block once for two or three q-blocks.
  *
  * Source: once the mask exists each head's load in sparse blocks is known
  * exactly and a few heavy heads set the critical path (aixai.ru FVAttn post,
@@ -234,7 +234,7 @@ int fvattn_route_pooled(const float* qbar, const float* kbar, int heads, int n, 
  *                            with FVATTN_SCHED_TILE_ORDER.
  * Bit-exact: there is exactly one correct result per input and flag.
  * Limits: 1 <= n_workers <= 2048; tile costs are clamped to [0, 65535];
- * heads*n_qblocks < 2^31; group in {1, 2} (else FVATTN_EINVAL).
+ * heads*n_qblocks < 2^31; group in {1, 2, 3} (else FVATTN_EINVAL).
  * workspace: at least fvattn_schedule_workspace_size() bytes.
  */
 size_t fvattn_schedule_workspace_size(int heads, int n_qblocks, int n_workers);
@@ -368,13 +368,18 @@ int fvattn_sasa_augment(const void* route_workspace, size_t route_workspace_byte
  *
  * scale <= 0 selects 1/sqrt(d).
  * v_layout: FVATTN_V_ROWS or FVATTN_V_TILES (see fvattn_pack_v); Q, K and O
- * are always [heads][n][d].  With FVATTN_V_TILES the V tiles must fit in 2 GiB
- * and block % 16 == 0 (else FVATTN_EUNSUPPORTED).
+ * are always [heads][n][d].  With FVATTN_V_TILES one head of V tiles
+ * (nB * block * d elements) must fit in 4 GiB and block % 16 == 0 (else
+ * FVATTN_EUNSUPPORTED); the tensors themselves have no size limit beyond
+ * n * d < 2^31.
  * kv_index entries must lie in [0, nB): the MFMA kernels clamp others into
  * that range, the plain kernel skips them (memory-safe, result undefined).
  * Work distribution (tiles of `group` q-blocks, numbered as in
  * fvattn_schedule; group 2 with FVATTN_V_TILES and an MFMA shape runs the
- * kernel that shares each K/V block between the two q-blocks):
+ * kernel that shares each K/V block between the two q-blocks; group 3, the
+ * same for three q-blocks, three wavefronts per SIMD, exists for bf16
+ * FVATTN_V_TILES with block 128 and d 64 or 128 only, else
+ * FVATTN_EUNSUPPORTED):
  *   worker_offsets != NULL: persistent launch of n_workers workgroups;
  *     workgroup w runs the tiles worker_tiles[worker_offsets[w] ..
  *     worker_offsets[w+1]) in order (the LPT lists of fvattn_schedule);
@@ -393,9 +398,9 @@ int fvattn_sasa_augment(const void* route_workspace, size_t route_workspace_byte
  *   kernel on `stream`) and the attention kernel updates it with atomics, so
  *   the caller only owns the memory, and calls that share it must not
  *   overlap.  Every tile still runs exactly once, in one workgroup, so the
- *   output is the same bits as without claims.  Honoured by the q-block-pair
- *   kernel (group 2, FVATTN_V_TILES, an MFMA shape); the other kernels run
- *   their lists as given.
+ *   output is the same bits as without claims.  Honoured by the kernels for
+ *   tiles of two or three q-blocks (group 2 or 3, FVATTN_V_TILES, an MFMA
+ *   shape); the other kernels run their lists as given.
  * claim_groups (0 <= x <= 64): 0 or 1 lets a workgroup claim from every
  *   list; x > 1 only from the lists w' with w' % x == w % x, so the worker
  *   groups of fvattn_schedule_heads stay independent, like ranks.

@@ -133,7 +133,7 @@ def _validation_main():
         (lib.fvattn_schedule_noalloc(P, 40, 591, 1, 2049, 0, P, P, P, P, N), EUNS),
         (lib.fvattn_schedule_noalloc(P, 40, 591, 1, 256, 2, P, P, P, P, N), EINVAL),
         (lib.fvattn_schedule_noalloc(N, 40, 591, 1, 256, 0, P, P, P, P, N), EINVAL),
-        (lib.fvattn_schedule_noalloc(P, 40, 591, 3, 256, 0, P, P, P, P, N), EINVAL),
+        (lib.fvattn_schedule_noalloc(P, 40, 591, 4, 256, 0, P, P, P, P, N), EINVAL),
         (lib.fvattn_schedule_noalloc(P, 40, 591, 1, 4, 8 << 8, P, P, P, P, N), EINVAL),
         (lib.fvattn_schedule_noalloc(P, 4097, 2, 1, 256, 8 << 8, P, P, P, P, N), EUNS),
         (lib.fvattn_schedule_noalloc(P, 64, 4096, 2, 256, 8 << 8, P, P, P, P, N),
@@ -144,8 +144,9 @@ def _validation_main():
         (lib.fvattn_sparse_attn(P, P, P, N, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 3, 1, 128, 64, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 256, 16, 0, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EUNS),
-        # tiled K/V one head past 2^31 bytes (17 heads x 4095 blocks of 128 x 128)
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 17, 4095 * 128, 128, 128, 1, 2, 0.0, P, P, N, N, 0, N, N, 0, N, N), EUNS),
+        # a head of 131072 blocks: its kv lists (nB^2 entries) pass 2^31 and
+        # are refused before the 4 GiB per-head bound of the V tiles applies
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, (1 << 24) - 1, 128, 128, 1, 2, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, float("inf"), P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, N, 4, N, N, 0, N, N), EINVAL),
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 0, 1, 0.0, P, P, P, P, 0, N, N, 0, N, N), EINVAL),
@@ -155,10 +156,17 @@ def _validation_main():
         (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 2, 1, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
         # workers
         (lib.fvattn_attn_workers(1, 128, 128, 1, 2, N), EINVAL),
-        (lib.fvattn_attn_workers(1, 128, 128, 1, 3, ctypes.byref(ctypes.c_int())), EINVAL),
+        (lib.fvattn_attn_workers(1, 128, 128, 1, 4, ctypes.byref(ctypes.c_int())), EINVAL),
+        (lib.fvattn_attn_workers(1, 128, 64, 1, 3, ctypes.byref(ctypes.c_int())), EUNS),
+        (lib.fvattn_attn_workers(1, 128, 128, 0, 3, ctypes.byref(ctypes.c_int())), EUNS),
         (lib.fvattn_attn_workers(1, 128, 128, 5, 1, ctypes.byref(ctypes.c_int())), EINVAL),
-        (lib.fvattn_schedule(P, 40, 591, 3, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
-        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 1, 3, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
+        (lib.fvattn_schedule(P, 40, 591, 4, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule(P, 40, 591, 0, 256, 1, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 1, 4, 0.0, P, P, N, N, 0, N, N, 0, N, N), EINVAL),
+        # three q-blocks per tile: bf16 V tiles of 128-key blocks only
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 128, 64, 16, 1, 3, 0.0, P, P, N, N, 0, N, N, 0, N, N), EUNS),
+        (lib.fvattn_sparse_attn(P, P, P, P, 1, 1, 256, 128, 128, 0, 3, 0.0, P, P, N, N, 0, N, N, 0, N, N), EUNS),
+        (lib.fvattn_sparse_attn(P, P, P, P, 0, 1, 256, 128, 128, 1, 3, 0.0, P, P, N, N, 0, N, N, 0, N, N), EUNS),
         # pack_v
         (lib.fvattn_pack_v(P, P, P, 1, 128, 64, 16, 1, N), EINVAL),
         (lib.fvattn_pack_v(P, ctypes.c_void_p(8192), P, 1, 128, 64, 16, 0, N), EUNS),
@@ -178,7 +186,7 @@ def _validation_main():
         (lib.fvattn_schedule_heads(P, 40, 591, 1, 256, 65, P, 0, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule_heads(P, 40, 591, 1, 4, 8, P, 0, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule_heads(P, 40, 591, 1, 256, 8, P, 8 << 8, P, P, P, P, P, 1 << 30, N), EINVAL),
-        (lib.fvattn_schedule_heads(P, 40, 591, 3, 256, 8, P, 0, P, P, P, P, P, 1 << 30, N), EINVAL),
+        (lib.fvattn_schedule_heads(P, 40, 591, 4, 256, 8, P, 0, P, P, P, P, P, 1 << 30, N), EINVAL),
         (lib.fvattn_schedule_heads(P, 40, 591, 1, 2049, 8, P, 0, P, P, P, P, P, 1 << 30, N), EUNS),
         (lib.fvattn_schedule_heads(P, 40, 591, 1, 256, 8, P, 0, P, P, P, P, P, 100, N), EWS),
         # SASA plan: thresholds and sizes

@@ -1,13 +1,14 @@
 """GPU regression test: run-time claims over runs of single-union-block tiles.
 
-With claims on, the persistent pair kernel posts claimed list positions in an
-LDS ring (its ordering is modelled on the CPU in test_claim_ring_model.py).
+With claims on, the persistent kernels for tiles of two or three q-blocks post
+claimed list positions in an LDS ring (its ordering is modelled on the CPU in test_claim_ring_model.py).
 Runs of consecutive tiles with a single union block are the case that needs
 that ordering: a Top-k floor of 0 or 1 makes them (the floor is optional
 protection, aixai.ru FVAttn post, "Sparse-routing frontend"), and so does a
-sequence no longer than one block (nB = 1).  Each case runs with one and two
-workers, with claims and with the static lists; the outputs must be equal bit
-for bit, and within the attention tolerance of the oracle.
+sequence no longer than one block (nB = 1).  Each case runs with tiles of two
+and of three q-blocks, with one and two workers, with claims and with the
+static lists; the outputs must be equal bit for bit, and within the attention
+tolerance of the oracle.
 """
 import numpy as np
 import pytest
@@ -37,9 +38,9 @@ def _lists(T, W, layout):
     return [tiles[0::2], tiles[1::2]]
 
 
-def _case(name):
-    """(H, n, kv_count, kv_index) of a hand-made case; tiles pair q-blocks
-    (2m, 2m + 1) of a head."""
+def _case(name, G):
+    """(H, n, kv_count, kv_index) of a hand-made case; tiles hold q-blocks
+    G*m .. G*m + G - 1 of a head."""
     if name == "nb1":
         H, n = 40, 100                          # one short block per head
         nb = 1
@@ -51,9 +52,10 @@ def _case(name):
     cnt = np.ones((H, nb), dtype=np.int32)
     idx = np.zeros((H, nb, nb), dtype=np.int32)
     for h in range(H):
-        for m in range(nb // 2):
-            j = (3 * h + 5 * m) % nb             # both q-blocks keep the same block
-            idx[h, 2 * m, 0] = idx[h, 2 * m + 1, 0] = j
+        for m in range((nb + G - 1) // G):
+            j = (3 * h + 5 * m) % nb             # the tile's q-blocks keep the same block
+            for i in range(G * m, min(nb, G * m + G)):
+                idx[h, i, 0] = j
     if name == "mixed":
         # single-block runs broken by a pair with nothing kept, a pair whose
         # halves keep one block each (two union blocks) and a longer pair
@@ -67,11 +69,12 @@ def _case(name):
 
 @pytest.mark.parametrize("name", ["single", "mixed", "nb1"])
 @pytest.mark.parametrize("W,layout", [(1, "one"), (2, "split"), (2, "one_sided")])
-def test_claims_over_single_block_tiles(name, W, layout):
-    say(f"claim ring {name} W={W} {layout}")
-    H, n, cnt, idx = _case(name)
+@pytest.mark.parametrize("G", [2, 3])
+def test_claims_over_single_block_tiles(name, W, layout, G):
+    say(f"claim ring {name} W={W} {layout} group={G}")
+    H, n, cnt, idx = _case(name, G)
     nb = cnt.shape[1]
-    tph = (nb + 1) // 2
+    tph = (nb + G - 1) // G
     g = torch.Generator().manual_seed(11)
     q = (torch.randn((H, n, D), generator=g) * 2).to(torch.bfloat16)
     k = (torch.randn((H, n, D), generator=g) * 2).to(torch.bfloat16)
@@ -90,7 +93,7 @@ def test_claims_over_single_block_tiles(name, W, layout):
     for use in (False, True):
         o = torch.full((H, n, D), float("nan"), dtype=torch.bfloat16, device=DEV)
         _lib.sparse_attn(qd, kd, vt, o, BLOCK, cnt_t, idx_t, off_t, wt_t, W,
-                         v_tiles=True, group=2, claims=claims if use else None)
+                         v_tiles=True, group=G, claims=claims if use else None)
         torch.cuda.synchronize()
         outs.append(o)
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))

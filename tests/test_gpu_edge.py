@@ -78,11 +78,16 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("name,w", SHAPES, ids=[s[0] for s in SHAPES])
-@pytest.mark.parametrize("ranks", [0, 2])
-def test_every_mfma_shape(name, w, ranks):
-    say(f"shape {name}: grid {w.grid}, d={w.d}, block={w.block}, ranks={ranks}")
+@pytest.mark.parametrize("ranks,group", [(0, None), (2, None), (0, 3), (2, 3)])
+def test_every_mfma_shape(name, w, ranks, group):
+    if group == 3 and w.block != 128:
+        pytest.skip("tiles of three q-blocks exist for 128-key blocks only")
+    say(f"shape {name}: grid {w.grid}, d={w.d}, block={w.block}, ranks={ranks}, "
+        f"group={group}")
     q, k, v, _ = synth.make_inputs(w, DEV)
     kw = dict(ranks=ranks, n_workers=8) if ranks else {}
+    if group:
+        kw["group"] = group
     path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, device=DEV, **kw)
     out = path.run(q, k, v, w.p, w.k)
     torch.cuda.synchronize()
@@ -90,5 +95,6 @@ def test_every_mfma_shape(name, w, ranks):
     check_route(path, w, w.p, range(w.heads), q, k)
     if not ranks:
         check_schedule(path)
+    assert path.group == (group or 2)
     tiles = [(h, i) for h in range(w.heads) for i in range(path.nb)]
     check_attention(path, w, q, k, v, out, tiles)

@@ -34,12 +34,12 @@ def head_f64(x, h):
     return x[h].float().cpu().numpy().astype(np.float64)
 
 
-def run_full(w, p=None, seed=None, r_override=None):
+def run_full(w, p=None, seed=None, r_override=None, group=None):
     p = w.p if p is None else p
     if seed is not None:
         w = w.with_(seed=seed)
     q, k, v, _ = synth.make_inputs(w, DEV, r_override=r_override)
-    path = FVAttnPath(w.heads, w.grid, w.d, w.block, device=DEV)
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, device=DEV, group=group)
     out = path.run(q, k, v, p, w.k)
     torch.cuda.synchronize()
     return path, q, k, v, out, p
@@ -143,11 +143,13 @@ def check_attention(path, w, q, k, v, out, tiles):
     say(f"  attention on {len(tiles)} sampled tiles: worst {worst}")
 
 
-@pytest.mark.parametrize("name", ["480p", "720p", "720p_sparse"])
-def test_fullsize_path(name):
+@pytest.mark.parametrize("name,group", [("480p", None), ("720p", None), ("720p_sparse", None),
+                                        ("720p", 2), ("720p", 3), ("720p_sparse", 3)])
+def test_fullsize_path(name, group):
     w = synth.WORKLOADS[name]
-    say(f"full-size path {name}: {w.heads} heads, grid {w.grid}, block {w.block}")
-    path, q, k, v, out, p = run_full(w)
+    say(f"full-size path {name}: {w.heads} heads, grid {w.grid}, block {w.block}, "
+        f"group {group}")
+    path, q, k, v, out, p = run_full(w, group=group)
     say(f"  workers {path.n_workers}, group {path.group}, v_tiles {path.v_tiles}")
     perm, inv = ohb.hilbert_order(*w.grid)
     assert np.array_equal(path.perm.cpu().numpy(), perm)

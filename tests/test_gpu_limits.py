@@ -1,13 +1,16 @@
-"""Attention at the largest tensors the C ABI accepts for the tiled-V kernel.
+"""Attention on tiled-V tensors larger than 2 GiB.
 
-K and V tiles are addressed with 32-bit buffer offsets, so the ABI takes at
-most 2^31 - 1 bytes per tensor (one head more is refused; `test_abi.py`).
-Here: 16 heads x 4095 key blocks of 128 x 128 in bf16, 2,146,959,360 bytes per
-tensor, with a ragged last block.  Each q-block keeps itself and a mirrored
-block (one block where the two coincide), so the last head's tail block, the
-highest offsets of every tensor, is read.  Grid launch and the persistent
-launch with LPT lists and run-time claims; sampled tiles against the plain
-float64 definition of attention on the kept rows.
+The tiled-V kernels address K and V one head at a time (a buffer descriptor
+per head, 32-bit byte offsets inside it), so a tensor may exceed 2^31 bytes;
+only one head of V tiles must fit in 4 GiB (`test_abi.py` checks the refusal
+past it).  Here: 17 heads x 4095 key blocks of 128 x 128 in bf16,
+2,281,138,560 bytes per tensor, one head past the 2^31 - 1 bytes that a
+single 32-bit offset over the whole tensor could reach, with a ragged last
+block.  Each q-block keeps itself and a mirrored block (one block where the
+two coincide), so the last head's tail block, the highest offsets of every
+tensor, is read.  Grid launch and the persistent launch with LPT lists and
+run-time claims; sampled tiles against the plain float64 definition of
+attention on the kept rows.
 """
 import numpy as np
 import pytest
@@ -20,7 +23,7 @@ from tests.parity import TOL, attn_errors
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-H, NB, BLOCK, D = 16, 4095, 128, 128
+H, NB, BLOCK, D = 17, 4095, 128, 128
 N = NB * BLOCK - 37
 
 
@@ -48,9 +51,9 @@ def rows(x, h, blocks):
 
 
 @pytest.mark.parametrize("mode", ["grid", "persistent"])
-def test_attention_at_the_largest_tiled_tensor(mode):
-    assert H * NB * BLOCK * D * 2 <= 0x7FFFFFFF < (H + 1) * NB * BLOCK * D * 2
-    say(f"largest tiled tensor: {H} heads, n={N}, {mode}")
+def test_attention_on_tiled_tensors_past_2gib(mode):
+    assert (H - 1) * NB * BLOCK * D * 2 <= 0x7FFFFFFF < H * NB * BLOCK * D * 2
+    say(f"tiled tensors past 2 GiB: {H} heads, n={N}, {mode}")
     g = torch.Generator(device=DEV).manual_seed(11)
     q = torch.randn((H, N, D), generator=g, device=DEV, dtype=torch.bfloat16)
     k = torch.randn((H, N, D), generator=g, device=DEV, dtype=torch.bfloat16)

@@ -144,6 +144,14 @@ def workload(name):
     if name == "mid_bf16_64":
         return synth.Workload("mid_bf16_64", 2, 64, (3, 10, 13), 64, 0.9, 4, "bf16",
                               s_range=(2.0, 128.0))
+    if name == "mid8_bf16":
+        # 8 blocks of 128 (4-row tail): tiles of three q-blocks end in a pair
+        return synth.Workload("mid8_bf16", 3, 128, (5, 9, 20), 128, 0.9, 4, "bf16",
+                              s_range=(4.0, 256.0))
+    if name == "mid7_bf16_64":
+        # d = 64, 7 blocks of 128 (102-row tail): the last tile of three holds one
+        return synth.Workload("mid7_bf16_64", 2, 64, (3, 10, 29), 128, 0.9, 4, "bf16",
+                              s_range=(2.0, 128.0))
     raise KeyError(name)
 
 
@@ -227,7 +235,7 @@ SCHED_CASES = [
 
 
 @pytest.mark.parametrize("xg", [1, 8, 3])
-@pytest.mark.parametrize("group", [1, 2])
+@pytest.mark.parametrize("group", [1, 2, 3])
 @pytest.mark.parametrize("tile_order", [False, True])
 @pytest.mark.parametrize("name,costs,W", SCHED_CASES)
 def test_schedule_bit_exact(name, costs, W, tile_order, group, xg):
@@ -247,9 +255,13 @@ def test_schedule_bit_exact(name, costs, W, tile_order, group, xg):
     elif name == "max_heads":
         costs = rng.integers(0, 50, size=(4096, 3))
     elif name == "huge_loads":
-        # pair tiles stay inside the 65535 cost clamp of the schedule ABI
-        costs = rng.integers(32000, 32768, size=(3, 2100))
+        # tiles stay inside the 65535 cost clamp of the schedule ABI
+        if group == 3:
+            costs = rng.integers(21000, 21845, size=(3, 3300))
+        else:
+            costs = rng.integers(32000, 32768, size=(3, 2100))
         assert costs.sum(1).min() >= 2 ** 26
+        assert olpt.group_costs(costs, group).max() <= 65535
     got = gpu_schedule(costs, W, tile_order, group, X)
     gc = olpt.group_costs(costs, group)
     if X > 1:
@@ -294,6 +306,38 @@ def test_attention_parity(name, balanced, v_tiles, group):
     assert np.array_equal(to_np(path.oh), ort.permute_rows(to_np(out), perm))
 
 
+@pytest.mark.parametrize("name", ["mid_bf16", "mid8_bf16", "mid7_bf16_64"])
+@pytest.mark.parametrize("balanced", [True, False])
+def test_attention_parity_three_qblocks(name, balanced):
+    """Tiles of three q-blocks (group 3, V tiles, 128-key blocks), with the
+    last tile of a head holding three, two or one q-blocks."""
+    w = workload(name)
+    say(f"attention group 3 {name} balanced={balanced}")
+    q, k, v, _ = synth.make_inputs(w, "cpu")
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, dtype=q.dtype, n_workers=5,
+                      device=DEV, group=3)
+    assert path.v_tiles and path.group == 3
+    out = path.run(q.to(DEV), k.to(DEV), v.to(DEV), w.p, w.k, balanced=balanced)
+    torch.cuda.synchronize()
+    perm = path.perm.cpu().numpy()
+    qh, kh, vh = (ort.permute_rows(to_np(x).astype(np.float64), perm) for x in (q, k, v))
+    ref = oat.unpermute_rows(oat.block_sparse_attention(
+        qh, kh, vh, w.block, path.kv_count.cpu().numpy(), path.kv_index.cpu().numpy()), perm)
+    err = attn_errors(to_np(out), ref)
+    say(f"  {err}")
+    tol = TOL[w.dtype]
+    assert err["max_abs"] <= tol["max_abs"] and err["rel_l2"] <= tol["rel_l2"], err
+    if balanced:
+        # the schedule of three-q-block tiles against the oracle
+        gc = olpt.group_costs(path.kv_count.cpu().numpy(), 3)
+        ref_s = olpt.lpt_schedule(gc, path.n_workers) if path.worker_groups == 1 else \
+            olpt.lpt_schedule_grouped(gc.reshape(w.heads, -1), path.n_workers,
+                                      path.worker_groups)
+        for g, r in zip((path.lpt_order, path.worker_offsets, path.worker_tiles,
+                         path.worker_load), ref_s):
+            assert np.array_equal(g.cpu().numpy(), r)
+
+
 @pytest.mark.parametrize("name", ["small", "mid_bf16", "ragged_f32"])
 def test_dense_control_matches_brute_force(name):
     """p = 1 keeps every block: the path must equal plain dense attention in
@@ -328,7 +372,8 @@ def attn_call(q, k, v, o, block, cnt, idx, v_tiles, group=1, **kw):
     (torch.bfloat16, 128, 128, True, 2), (torch.bfloat16, 128, 128, True, 1),
     (torch.bfloat16, 128, 128, False, 1), (torch.bfloat16, 64, 64, True, 2),
     (torch.bfloat16, 64, 64, False, 2), (torch.bfloat16, 64, 16, True, 1),
-    (torch.float32, 64, 16, False, 2)])
+    (torch.float32, 64, 16, False, 2), (torch.bfloat16, 128, 128, True, 3),
+    (torch.bfloat16, 64, 128, True, 3)])
 def test_attention_handmade_lists(dtype, d, block, v_tiles, group):
     """Edge cases: an empty row (written as zeros), a single kept block, only
     the short tail block, a pair whose two lists differ, and constant V."""
@@ -374,22 +419,23 @@ def test_attention_handmade_lists(dtype, d, block, v_tiles, group):
 
 
 @pytest.mark.parametrize("layout", ["one_list", "round_robin", "reversed", "more_workers"])
-def test_runtime_claims(layout):
+@pytest.mark.parametrize("group", [2, 3])
+def test_runtime_claims(layout, group):
     """Run-time balancing: with claim counters the workgroups take tiles from
     other workers' lists; every tile still runs once, in one workgroup, so the
-    output equals the static-list run bit for bit.  Includes a pair with
+    output equals the static-list run bit for bit.  Includes a tile with
     nothing kept (zeroed by the claiming workgroup)."""
-    w = workload("mid_bf16")
-    say(f"runtime claims {layout}")
+    w = workload("mid_bf16" if group == 2 else "mid8_bf16")
+    say(f"runtime claims {layout} group={group}")
     q, k, v, _ = synth.make_inputs(w, "cpu")
-    path = FVAttnPath(w.heads, w.grid, w.d, w.block, device=DEV)
-    assert path.group == 2 and path.v_tiles
+    path = FVAttnPath(w.heads, w.grid, w.d, w.block, device=DEV, group=group)
+    assert path.group == group and path.v_tiles
     path.order()
     path.to_hilbert(q.to(DEV), k.to(DEV), v.to(DEV))
     path.route(w.p, w.k)
     cnt = path.kv_count.clone()
-    cnt[1, 2:4] = 0                                 # head 1, pair 1: nothing kept
-    tph = (path.nb + 1) // 2
+    cnt[1, group:2 * group] = 0                     # head 1, tile 1: nothing kept
+    tph = (path.nb + group - 1) // group
     T = w.heads * tph
     tiles = list(range(T))
     if layout == "one_list":
@@ -410,13 +456,13 @@ def test_runtime_claims(layout):
     for use in (False, True):
         path.oh.fill_(float("nan"))
         _lib.sparse_attn(path.qh, path.kh, path.vh, path.oh, w.block, cnt, path.kv_index,
-                         off_t, wt_t, W, v_tiles=True, group=2,
+                         off_t, wt_t, W, v_tiles=True, group=group,
                          claims=claims if use else None)
         torch.cuda.synchronize()
         outs.append(path.oh.clone())
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     got = to_np(outs[1])
-    assert (got[1, 2 * w.block:4 * w.block] == 0).all()
+    assert (got[1, group * w.block:2 * group * w.block] == 0).all()
     c = claims.cpu().numpy()
     assert (c >= np.diff(off)).all()                 # every list was drained
     perm = path.perm.cpu().numpy()
@@ -470,7 +516,7 @@ def test_attn_workers_is_a_multiple_of_the_cus():
     say("attn_workers")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for v_tiles in (True, False):
-        for group in (1, 2):
+        for group in (1, 2, 3) if v_tiles else (1, 2):
             w = _lib.attn_workers(torch.bfloat16, 128, 128, v_tiles, group)
             assert w >= cus and w % cus == 0
     assert _lib.attn_workers(torch.float32, 64, 16, False) % cus == 0
