@@ -16,6 +16,9 @@
 //                  row loads, per-lane column sums, LDS reduction.  HBM-bound:
 //                  reads Q and K exactly once.
 //   score_kernel   z = qbar kbar^T * scale per head, LDS-tiled 64x64 fp32.
+//   select_wave_kernel  one wavefront per row for nB <= 2048, four rows per
+//                  workgroup: the same arithmetic as select_kernel (so the
+//                  same output bytes) with no workgroup barrier.
 //   select_kernel  one workgroup per (query block, head): row softmax, bitonic
 //                  sort of (P, ~j) keys held in registers (partners in the
 //                  same thread swap in place, partners in the wavefront come
@@ -367,6 +370,186 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
   if (tid == 0) kv_count[row] = n_keep;
 }
 
+// One wavefront per row, four rows per workgroup, for np <= 2048 (nB <=
+// 2048): the same arithmetic as select_kernel, so the same output bytes, with
+// no workgroup barrier.  Virtual thread t of select_kernel's 256 (its row
+// max, row-sum partial and prefix chunk) lives in lane t % 64 of this
+// wavefront, so lane l holds the sums of t = l, l+64, l+128, l+192 and the
+// sorted ranks KW*l .. KW*l + KW - 1, which are select_kernel's prefix chunks
+// 4l .. 4l+3 (np/256 ranks each).  The bitonic network runs in registers
+// (partners within a lane) and by lane shuffles (partners in other lanes).
+// Per wavefront LDS: the row's exponentials (np floats) and the kept flags
+// (np bytes).
+constexpr int kWaveRows = 4;
+
+template <int KW>
+__global__ __launch_bounds__(kWave * kWaveRows) void select_wave_kernel(
+    const float* __restrict__ z, int nb, int rows, float p, int k_floor,
+    uint8_t* __restrict__ mask, int32_t* __restrict__ kv_count,
+    int32_t* __restrict__ kv_index) {
+  constexpr int NP = KW * kWave;                 // padded row length (power of two)
+  constexpr int PER = NP / kSelectThreads;       // select_kernel's prefix chunk
+  static_assert(PER * 4 == KW, "four prefix chunks per lane");
+  __shared__ float s_e[kWaveRows][NP];
+  __shared__ uint8_t s_flag[kWaveRows][NP];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int row = blockIdx.x * kWaveRows + wv;
+  if (row >= rows) return;                       // whole wavefront; no barrier below
+  const float* zr = z + (size_t)row * nb;
+  float* e_row = s_e[wv];
+  uint8_t* flag = s_flag[wv];
+
+  // row max (order-free), then the row sum in select_kernel's order: virtual
+  // thread t = 64w + l adds j = t, t + 256, ... in ascending j; each
+  // wavefront of virtual threads reduces by an xor butterfly; the four
+  // results add in wavefront order
+  float mx = -INFINITY;
+  for (int j = lane; j < nb; j += kWave) mx = fmaxf(mx, zr[j]);
+  mx = wave_max(mx);
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    for (int j = kWave * w + lane; j < nb; j += kSelectThreads) {
+      const float e = expf(zr[j] - mx);
+      e_row[j] = e;
+      part[w] += e;
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) part[w] += __shfl_xor(part[w], off, kWave);
+  }
+  const float sum = ((part[0] + part[1]) + part[2]) + part[3];
+
+  uint64_t kr[KW];
+#pragma unroll
+  for (int e = 0; e < KW; ++e) {
+    const int j = KW * lane + e;
+    kr[e] = j < nb ? ((uint64_t)__float_as_uint(e_row[j] / sum) << 32) | (uint64_t)(~(uint32_t)j)
+                   : 0;
+  }
+  // bitonic sort, descending.  Keys are unique, so the result is the order
+  // select_kernel produces.  Ranks x = KW*lane + e; a stage (kk, jj) pairs x
+  // with x ^ jj and the pair's lower rank takes the larger key where
+  // (x & kk) == 0.  kk <= KW: lane-local stages, unrolled (the direction is a
+  // constant, or the lane's parity at kk = KW); kk > KW: partners in other
+  // lanes (jj >= KW, by shuffle) or in this lane (jj < KW), the direction a
+  // per-lane constant of the stage.
+  auto ce = [&](int e0, int e1, bool desc) {
+    // order kr[e0] >= kr[e1] when desc, else kr[e0] <= kr[e1]
+    const uint64_t a = kr[e0], b = kr[e1];
+    const bool sw = (a < b) == desc;
+    kr[e0] = sw ? b : a;
+    kr[e1] = sw ? a : b;
+  };
+#pragma unroll
+  for (int kk = 2; kk <= KW; kk <<= 1) {
+    const bool lane_desc = kk < KW ? true : (lane & 1) == 0;
+#pragma unroll
+    for (int jr = kk >> 1; jr >= 1; jr >>= 1) {
+#pragma unroll
+      for (int e = 0; e < KW; ++e)
+        if ((e & jr) == 0) ce(e, e | jr, kk < KW ? (e & kk) == 0 : lane_desc);
+    }
+  }
+#pragma unroll 1
+  for (int kk = 2 * KW; kk <= NP; kk <<= 1) {
+    const bool desc = ((KW * lane) & kk) == 0;
+#pragma unroll 1
+    for (int jj = kk >> 1; jj >= KW; jj >>= 1) {
+      const int lanes = jj / KW;
+      // the lower rank of each pair keeps the larger key where desc
+      const bool keep_max = (((KW * lane) & jj) == 0) == desc;
+#pragma unroll
+      for (int e = 0; e < KW; ++e) {
+        const uint64_t mine = kr[e];
+        const uint64_t other = (uint64_t)__shfl_xor((long long)mine, lanes, kWave);
+        kr[e] = ((other > mine) == keep_max) ? other : mine;
+      }
+    }
+#pragma unroll
+    for (int jr = KW / 2; jr >= 1; jr >>= 1) {
+#pragma unroll
+      for (int e = 0; e < KW; ++e)
+        if ((e & jr) == 0) ce(e, e | jr, desc);
+    }
+  }
+
+  // prefix sums in select_kernel's order: PER ranks per chunk summed in
+  // order, chunk bases accumulated left to right over all 256 chunks (the
+  // chunks of lane 0, then lane 1, ...), carried from lane to lane
+  float cum[KW], tot[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float run = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      run += __uint_as_float((uint32_t)(kr[PER * c + e] >> 32));
+      cum[PER * c + e] = run;
+    }
+    tot[c] = run;
+  }
+  float base[4] = {0.f, 0.f, 0.f, 0.f};
+  {
+    float b = 0.f;                                 // wave-uniform running base
+#pragma unroll 1
+    for (int l = 0; l < kWave; ++l) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float t = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tot[c]), l));
+        if (lane == l) base[c] = b;
+        b += t;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) cum[PER * c + e] += base[c];
+  }
+
+  int n_p = nb;
+  if (p < 1.0f) {
+    int first = nb;
+#pragma unroll
+    for (int e = KW - 1; e >= 0; --e) {
+      const int x = KW * lane + e;
+      if (x < nb && cum[e] >= p) first = x;
+    }
+    first = wave_min(first);
+    n_p = first < nb ? first + 1 : nb;
+  }
+  const int n_keep = min(nb, max(n_p, k_floor));
+
+  for (int j = lane; j < NP; j += kWave) flag[j] = 0;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int e = 0; e < KW; ++e)
+    if (KW * lane + e < n_keep) flag[~(uint32_t)(kr[e] & 0xffffffffu)] = 1;
+  __builtin_amdgcn_wave_barrier();
+
+  uint8_t* mrow = mask + (size_t)row * nb;
+  for (int j = lane; j < nb; j += kWave) mrow[j] = flag[j];
+  // ascending compaction: contiguous chunks of j per lane, wavefront scan
+  const int perj = (nb + kWave - 1) / kWave;
+  const int j0 = lane * perj;
+  int mine = 0;
+  for (int e = 0; e < perj; ++e) {
+    const int j = j0 + e;
+    if (j < nb) mine += flag[j];
+  }
+  int pos = wave_inclusive_scan(mine) - mine;
+  int32_t* irow = kv_index + (size_t)row * nb;
+  for (int e = 0; e < perj; ++e) {
+    const int j = j0 + e;
+    if (j < nb && flag[j]) irow[pos++] = j;
+  }
+  if (lane == 0) kv_count[row] = n_keep;
+}
+
 __global__ __launch_bounds__(256) void load_kernel(
     const int32_t* __restrict__ kv_count, int nb, int64_t* __restrict__ head_load,
     float* __restrict__ head_density) {
@@ -459,6 +642,33 @@ hipError_t launch_route_pooled(const float* qbar, const float* kbar, int heads, 
   int np = 1;
   while (np < nb) np <<= 1;
   if (np < kSelectThreads) np = kSelectThreads;
+  if (np <= 2048) {
+    // one wavefront per row (same output bytes as select_kernel)
+    const int rows = heads * nb;
+    const dim3 wgrid((rows + kWaveRows - 1) / kWaveRows);
+    const dim3 wblock(kWave * kWaveRows);
+    switch (np) {
+      case 256:
+        hipLaunchKernelGGL(select_wave_kernel<4>, wgrid, wblock, 0, s, ws.z, nb, rows, p,
+                           k_floor, mask, kv_count, kv_index);
+        break;
+      case 512:
+        hipLaunchKernelGGL(select_wave_kernel<8>, wgrid, wblock, 0, s, ws.z, nb, rows, p,
+                           k_floor, mask, kv_count, kv_index);
+        break;
+      case 1024:
+        hipLaunchKernelGGL(select_wave_kernel<16>, wgrid, wblock, 0, s, ws.z, nb, rows, p,
+                           k_floor, mask, kv_count, kv_index);
+        break;
+      default:
+        hipLaunchKernelGGL(select_wave_kernel<32>, wgrid, wblock, 0, s, ws.z, nb, rows, p,
+                           k_floor, mask, kv_count, kv_index);
+        break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_head_load(kv_count, heads, nb, head_load, head_density, s);
+  }
   const size_t lds = (size_t)np * (sizeof(uint64_t) + sizeof(float) + sizeof(int32_t));
   const dim3 grid(nb, heads);
   switch (np / kSelectThreads) {

@@ -7,8 +7,9 @@ library:
     permute_pool     Q, K -> Hilbert order, with the pooled block means in the
                      same pass (fused=False: permute_rows, pooling in route)
     pack_v           V -> Hilbert order, one transposed tile per key block; with
-                     overlap=True on a second stream, concurrent with routing
-                     and scheduling (V feeds neither), joined before attention
+                     overlap=True on a second stream, started once routing is
+                     queued so it runs beside the schedule (a few latency-bound
+                     workgroups; V feeds neither), joined before attention
     route_pooled     pooled-Q/K Top-p + Top-k -> mask, kept lists, head load
     [sasa_plan, sasa_augment   per-rank image only: head moves and extra
                      blocks on the groups off the critical path]
@@ -91,6 +92,7 @@ class FVAttnPath:
         self.overlap = overlap
         self.side = torch.cuda.Stream(device=dev) if overlap else None
         self._v_pending = False
+        self._v_src = None
         W = self.n_workers
         if worker_groups is None:
             # at least two heads per group, or the head-level LPT cannot balance
@@ -138,8 +140,19 @@ class FVAttnPath:
         if not self.overlap:
             self._layout_v(v)
             return
-        # the side stream first waits for all work queued so far on the main
-        # one: v is ready and the previous attention has finished reading vh
+        # with overlap the V layout starts after routing is queued (start_v)
+        self._v_src = v
+
+    def start_v(self):
+        """Queue the pending V layout on the side stream.  The side stream
+        first waits for all work queued so far on the main one (v is ready,
+        the previous attention has finished reading vh, routing is queued, so
+        the layout shares the card with the schedule rather than with the
+        bandwidth-heavy routing)."""
+        v = self._v_src
+        if v is None:
+            return
+        self._v_src = None
         main = torch.cuda.current_stream(self.device)
         self.side.wait_stream(main)
         with torch.cuda.stream(self.side):
@@ -163,7 +176,11 @@ class FVAttnPath:
         return self._vh
 
     def join(self):
-        """Make the main stream wait for the V layout (no-op without overlap)."""
+        """Make the main stream wait for the V layout (no-op without overlap);
+        a layout not yet started runs on the main stream."""
+        if self._v_src is not None:
+            v, self._v_src = self._v_src, None
+            self._layout_v(v)
         if self._v_pending:
             torch.cuda.current_stream(self.device).wait_stream(self.side)
             self._v_pending = False
@@ -173,9 +190,10 @@ class FVAttnPath:
             _lib.route_pooled(self.qbar, self.kbar, self.n, self.block, p, k_floor, self.mask,
                               self.kv_count, self.kv_index, self.head_load,
                               self.head_density, self.route_ws)
-            return
-        _lib.route(self.qh, self.kh, self.block, p, k_floor, self.mask, self.kv_count,
-                   self.kv_index, self.head_load, self.head_density, self.route_ws)
+        else:
+            _lib.route(self.qh, self.kh, self.block, p, k_floor, self.mask, self.kv_count,
+                       self.kv_index, self.head_load, self.head_density, self.route_ws)
+        self.start_v()
 
     def plan_ranks(self):
         """Per-rank image: mode, head moves and budgets; with sasa, the extra
