@@ -77,11 +77,15 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("name,w", SHAPES, ids=[s[0] for s in SHAPES])
-@pytest.mark.parametrize("ranks,group", [(0, None), (2, None), (0, 3), (2, 3)])
+# tiles of three q-blocks exist for 128-key blocks only
+SHAPE_PARAMS = [(name, w, ranks, group) for name, w in SHAPES
+                for ranks, group in [(0, None), (2, None), (0, 3), (2, 3)]
+                if group is None or w.block == 128]
+
+
+@pytest.mark.parametrize("name,w,ranks,group", SHAPE_PARAMS,
+                         ids=[f"{p[0]}-r{p[2]}-g{p[3] or 2}" for p in SHAPE_PARAMS])
 def test_every_mfma_shape(name, w, ranks, group):
-    if group == 3 and w.block != 128:
-        pytest.skip("tiles of three q-blocks exist for 128-key blocks only")
     say(f"shape {name}: grid {w.grid}, d={w.d}, block={w.block}, ranks={ranks}, "
         f"group={group}")
     q, k, v, _ = synth.make_inputs(w, DEV)
