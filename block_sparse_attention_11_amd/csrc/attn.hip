@@ -7,11 +7,9 @@
 // blocks, evaluated block by block with an online (running max / running
 // sum) softmax in fp32.
 //
-// Two kernels:
-//
-// attn_mfma_kernel<D, BLK>  bf16 storage, MFMA v_mfma_f32_32x32x16_bf16.
-//   A workgroup owns one query block of BLK rows with BLK/32 wavefronts; each
-//   wavefront owns 32 queries.  Everything is computed transposed,
+// The MFMA formulation, shared by the three bf16 kernels (storage bf16,
+// v_mfma_f32_32x32x16_bf16, each wavefront owns 32 queries).  Everything is
+// computed transposed,
 //       S^T[key][q] = K Q^T      (A = K rows from LDS, B = Q from registers)
 //       O^T[d][q]  += V^T P^T    (A = V^T rows from LDS, B = P from registers)
 //   so in both accumulators lane l holds query l%32: the row max and row sum
@@ -20,16 +18,27 @@
 //   (the 16-key chunks are taken in the order the accumulator layout gives;
 //   V^T is read from LDS in that same order).  K is staged in LDS row-major
 //   with an XOR swizzle of its 16-byte chunks, V transposed with an XOR
-//   swizzle of its 8-byte units, both conflict-free for the MFMA reads.
-//   The softmax runs in the exp2 domain with scale*log2(e) folded into one
-//   FMA per score; P is rounded to bf16 (round to nearest even) for the PV
-//   product.
+//   swizzle (of 8-byte units in attn_mfma_kernel, of 16-byte chunks in the
+//   two copy kernels), conflict-free for the MFMA reads.  The softmax runs in
+//   the exp2 domain with scale*log2(e) folded into one FMA per score; P is
+//   rounded to bf16 (round to nearest even) for the PV product.
 //
+// Kernels:
+//
+// attn_mfma_tile_kernel<D, BLK, G, HK>  the default: persistent workgroups of
+//   G consecutive q-blocks (G = 2, or 3) that walk the union of their kept
+//   lists, with K and V^T key-block tiles copied into LDS by buffer loads
+//   straight to LDS, double buffered, one barrier per key block, and
+//   run-time tile claims.
+// attn_mfma_dma_kernel<D, BLK>  the same copies for one q-block per
+//   workgroup (BLK/32 wavefronts).
+// attn_mfma_kernel<D, BLK>  one q-block per workgroup, V in row layout,
+//   staged through registers.
 // attn_simple_kernel<T, DMAX>  plain fp32 VALU reference kernel for every
 //   other shape (fp32 inputs, small head dims, odd block sizes): one thread
 //   per query row, K/V staged through LDS in chunks of 32 rows.
 //
-// Both run either persistently (workgroup w walks its LPT list) or as a
+// All run either persistently (workgroup w walks its LPT list) or as a
 // head-major grid (one workgroup per tile), and write per-workgroup
 // timestamps (s_memrealtime, 100 MHz) plus the HW_ID / XCC_ID registers.
 #include <math.h>
@@ -774,8 +783,9 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_mfma_dma_kernel(AttnArgs a) {
 // w % 4, so each SIMD holds one wavefront of every q-block).  K and V^T are double
 // buffered in four LDS arrays (the loop body is instantiated for both buffer
 // assignments, so the compiler sees distinct objects and does not wait on the
-// in-flight copy): the copy of union block u+1 is issued right after the one
-// barrier of block u and overlaps all of block u's work.  HK is the key
+// in-flight copy): the copy of union block u+1 is issued after the one barrier
+// of block u (by the wavefronts that compute on block u after their score
+// product, by the others at once) and overlaps block u's work.  HK is the key
 // width of one online-softmax step (the block is processed in BLK/HK steps).
 // ---------------------------------------------------------------------------
 // The persistent launch (worker lists) and the head-major grid launch (one
