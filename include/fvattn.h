@@ -374,6 +374,8 @@ int fvattn_sasa_augment(const void* route_workspace, size_t route_workspace_byte
  * n * d < 2^31.
  * kv_index entries must lie in [0, nB): the MFMA kernels clamp others into
  * that range, the plain kernel skips them (memory-safe, result undefined).
+ * kv_count entries above nB count as nB; entries of 0 or below leave the
+ * q-block's rows zero.
  * Work distribution (tiles of `group` q-blocks, numbered as in
  * fvattn_schedule; group 2 with FVATTN_V_TILES and an MFMA shape runs the
  * kernel that shares each K/V block between the two q-blocks; group 3, the
