@@ -893,9 +893,10 @@ __global__ __launch_bounds__(2 * G * BLK) void attn_mfma_tile_kernel(AttnArgs a)
 #pragma unroll
     for (int g2 = 0; g2 < G; ++g2) w.in |= (jg[g2] == w.u) << g2;
   };
-  // kept count of q-block i0 + g2 of head h (0 past the last q-block)
+  // kept count of q-block i0 + g2 of head h, clamped to [0, nb] (0 past the
+  // last q-block): a negative entry must not make the tile look empty
   auto count_at = [&](int h, int i0, int g2) {
-    return i0 + g2 < nb ? min(ld_uniform(a.kv_count + (size_t)h * nb + i0 + g2), nb) : 0;
+    return i0 + g2 < nb ? min(max(ld_uniform(a.kv_count + (size_t)h * nb + i0 + g2), 0), nb) : 0;
   };
   auto zero_rows = [&](int h, int i) {
     const int qr = i * BLK + wq * 32 + col;

@@ -102,3 +102,78 @@ def test_every_mfma_shape(name, w, ranks, group):
     assert path.group == (group or 2)
     tiles = [(h, i) for h in range(w.heads) for i in range(path.nb)]
     check_attention(path, w, q, k, v, out, tiles)
+
+
+@pytest.mark.parametrize("v_tiles,group,persist,use_claims",
+                         [(False, 1, True, False), (True, 1, True, False),
+                          (True, 2, True, False), (True, 2, True, True),
+                          (True, 2, False, False), (True, 3, True, True)])
+def test_counts_outside_range(v_tiles, group, persist, use_claims):
+    """kv_count entries above nB act as nB, entries of 0 or below leave the
+    q-block's rows zero, on every kernel the entry point can run (V rows,
+    V tiles on one q-block, tiles of two and three q-blocks; persistent with
+    and without claims, and the head-major grid).  The other rows must match
+    the oracle."""
+    from block_sparse_attention_11_amd import _lib
+    from oracle import attention as oat
+    from tests.parity import TOL, attn_errors
+    say(f"counts outside range: v_tiles={v_tiles} group={group} persist={persist} "
+        f"claims={use_claims}")
+    H, BLK, D = 3, 128, 128
+    n = 6 * BLK - 40
+    nb = 6
+    rng = np.random.default_rng(5)
+    cnt = rng.integers(1, nb + 1, size=(H, nb)).astype(np.int32)
+    cnt[0, 1] = -5
+    cnt[1, 4] = nb + 7
+    cnt[1, 5] = 0
+    cnt[2, 0] = cnt[2, 1] = -1             # a whole pair below zero
+    cnt[2, 3] = -(1 << 30)
+    idx = np.zeros((H, nb, nb), dtype=np.int32)
+    for h in range(H):
+        for i in range(nb):
+            c = int(np.clip(cnt[h, i], 0, nb))
+            idx[h, i, :c] = np.sort(rng.choice(nb, size=c, replace=False))
+            idx[h, i, c:] = rng.integers(0, nb, size=nb - c)   # unused, in range
+    g = torch.Generator().manual_seed(23)
+    q = (torch.randn((H, n, D), generator=g) * 2).to(torch.bfloat16)
+    k = (torch.randn((H, n, D), generator=g) * 2).to(torch.bfloat16)
+    v = torch.randn((H, n, D), generator=g).to(torch.bfloat16)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    if v_tiles:
+        vin = torch.empty((H, nb, D, BLK), dtype=torch.bfloat16, device=DEV)
+        _lib.pack_v(vd, vin, torch.arange(n, dtype=torch.int32, device=DEV), BLK)
+    else:
+        vin = vd
+    tph = (nb + group - 1) // group
+    T = H * tph
+    W = 2
+    off_t = wt_t = None
+    if persist:
+        lists = [list(range(T))[0::2], list(range(T))[1::2]]
+        off = np.zeros(W + 1, dtype=np.int32)
+        off[1:] = np.cumsum([len(x) for x in lists])
+        wt = np.array([t for x in lists for t in x], dtype=np.int32)
+        off_t, wt_t = torch.from_numpy(off).to(DEV), torch.from_numpy(wt).to(DEV)
+    claims = torch.zeros(W, dtype=torch.int32, device=DEV) if use_claims else None
+    o = torch.full((H, n, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    _lib.sparse_attn(qd, kd, vin, o, BLK, torch.from_numpy(cnt).to(DEV),
+                     torch.from_numpy(idx).to(DEV), off_t, wt_t, W if persist else 0,
+                     v_tiles=v_tiles, group=group, claims=claims)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    eff = np.clip(cnt, 0, nb)
+    for h in range(H):
+        for i in range(nb):
+            if eff[h, i] == 0:
+                assert (got[h, i * BLK:min(n, (i + 1) * BLK)] == 0).all(), (h, i, cnt[h, i])
+    kept = [(h, i) for h in range(H) for i in range(nb) if eff[h, i] > 0]
+    ref = oat.block_sparse_attention(q.float().numpy().astype(np.float64),
+                                     k.float().numpy().astype(np.float64),
+                                     v.float().numpy().astype(np.float64),
+                                     BLK, eff, idx, tiles=kept)
+    keep = ~np.isnan(ref)
+    assert not np.isnan(got[keep]).any()
+    err = attn_errors(got[keep], ref[keep])
+    tol = TOL["bf16"]
+    assert err["max_abs"] <= tol["max_abs"] and err["rel_l2"] <= tol["rel_l2"], err
