@@ -144,7 +144,9 @@ def check_attention(path, w, q, k, v, out, tiles):
 
 
 @pytest.mark.parametrize("name,group", [("480p", None), ("720p", None), ("720p_sparse", None),
-                                        ("720p", 2), ("720p", 3), ("720p_sparse", 3)])
+                                        ("720p", 2), ("720p", 3), ("720p_sparse", 3),
+                                        ("480p", 3), ("720p_rank", None),
+                                        ("long720p_sparse", None)])
 def test_fullsize_path(name, group):
     w = synth.WORKLOADS[name]
     say(f"full-size path {name}: {w.heads} heads, grid {w.grid}, block {w.block}, "
